@@ -1,0 +1,215 @@
+"""Benchmark of libh3qk on one MI355X.
+
+One step = one pass of the fused RMSNorm + 3-axis RoPE + head-major permute over the full-latent
+workload (token grid 62x48x84, T = 249,984, H = 16, D = 64, fp16 fused QKV [1, 249984, 3072] ->
+Q fp32, K/V fp16 head-major), inputs resident in HBM, launched through the C ABI on torch's
+current stream.  Prints one JSON line: throughput in algorithmic GB/s (read every input element
+once, write every output element once), tokens/ms, the roofline fraction of the fused kernel
+(HIP events around every launch in the timed region) and the CPU oracle timed on a bounded sample
+of the same workload.  --extra adds the one-tile, eight-tile and FP8 long-sequence (amax + cast)
+passes as extra lines of the same object.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused QK-norm+RoPE+permute GB/s and tokens/ms; % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_latent.txt")
+KERNEL_SRC = os.path.join(ROOT, "rmsnorm_rope_amd", "csrc", "h3qk_kernels.hip")
+
+
+def kernel_digest() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, when it was taken on the
+    current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if "=" in ln and not ln.startswith("#"):
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sha256_16") != kernel_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(launch, steps, warmup, stream):
+    """Run `launch` warmup + steps times on `stream`; returns (total ms over the timed region,
+    mean per-launch ms from event pairs around each launch)."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [a.elapsed_time(b) for a, b in ev]
+    return total, sum(per) / len(per)
+
+
+def cpu_baseline(pb, budget_s=12.0):
+    """The oracle (plain single-threaded C) on the first tokens of the same workload, growing the
+    sample until about budget_s seconds of CPU work."""
+    import dataclasses
+
+    import oracle
+    from synth.problem import algorithmic_bytes, oracle_spec
+    wl = pb.wl
+    x = pb.qkv_host()
+    oracle.lib()
+    ts, spent, tokens = 4096, 0.0, 0
+    while True:
+        sub = dataclasses.replace(wl, T=ts, valid=[ts] * wl.B)
+        t = time.perf_counter()
+        oracle.qk_rmsnorm_rope_permute(oracle_spec(sub), x[:, :ts], wl.in_dtype, pb.wq_host, pb.wk_host, "f32", "f16")
+        dt = time.perf_counter() - t
+        spent, tokens = dt, ts
+        if dt >= budget_s / 3 or ts >= wl.T:
+            break
+        ts = min(wl.T, int(ts * max(2.0, budget_s / 3 / max(dt, 1e-3))))
+    sub = dataclasses.replace(wl, T=tokens, valid=[tokens] * wl.B)
+    nbytes = algorithmic_bytes(sub, "store")
+    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_ms": round(tokens * wl.B / spent / 1e3, 2), "seconds": round(spent, 2),
+            "sample": f"first {tokens} of {wl.T} tokens of the {wl.name} workload (all {wl.H} heads, Q f32, K/V f16), "
+                      f"single-threaded C oracle"}
+
+
+def bench_store(wl, steps, warmup, rotate=1):
+    import torch
+
+    from synth.problem import DeviceProblem, algorithmic_bytes
+    pbs = [DeviceProblem(wl, "cuda") for _ in range(rotate)]
+    outs = [(pb.out("f32"), pb.out("f16"), pb.out(wl.in_dtype)) for pb in pbs]
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def launch():
+        j = it[0] % rotate
+        it[0] += 1
+        pbs[j].run_store("f32", "f16", outs=outs[j], stream=stream.cuda_stream)
+
+    total, per = time_launches(launch, steps, warmup, stream)
+    nbytes = algorithmic_bytes(wl, "store")
+    return pbs[0], {"ms_per_step": total / steps, "kernel_ms": per, "bytes": nbytes}
+
+
+def bench_fp8(wl, steps, warmup):
+    import torch
+
+    from synth.problem import DeviceProblem, algorithmic_bytes
+    pb = DeviceProblem(wl, "cuda")
+    amax = torch.empty(2, dtype=torch.float32, device="cuda")
+    outs = (pb.out("e4m3"), pb.out("e4m3"), pb.out(wl.in_dtype), torch.empty(2, dtype=torch.float32, device="cuda"))
+    stream = torch.cuda.current_stream()
+    ta, pa = time_launches(lambda: pb.run_amax(amax, stream=stream.cuda_stream), steps, warmup, stream)
+    tc, pc = time_launches(lambda: pb.run_cast(amax, outs=outs, stream=stream.cuda_stream), steps, warmup, stream)
+    ba, bc = algorithmic_bytes(wl, "amax"), algorithmic_bytes(wl, "cast")
+    return {"amax_us": round(pa * 1e3, 2), "amax_GBs": round(ba / pa / 1e6, 1),
+            "cast_us": round(pc * 1e3, 2), "cast_GBs": round(bc / pc / 1e6, 1),
+            "pair_us": round((pa + pc) * 1e3, 2), "pair_GBs": round((ba + bc) / (pa + pc) / 1e6, 1),
+            "pair_frac_of_peak": round((ba + bc) / (pa + pc) / 1e6 / HBM_PEAK_GBS, 4),
+            "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1)}
+
+
+def copy_calibration(nbytes=1 << 31, steps=10):
+    """A plain device copy of known size (torch's copy kernel), for scaling the PMC byte counters."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also time the tile, eight-tile and FP8 workloads")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (one process, one MI355X); "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from rmsnorm_rope_amd import _build
+    if _build.stale():
+        _build.build()
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    wl = synth.workloads()["latent"]
+    pb, r = bench_store(wl, args.steps, args.warmup)
+    nbytes = r["bytes"]
+    value = nbytes / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = nbytes / (r["kernel_ms"] * 1e-3) / 1e9
+    tokens = wl.B * wl.T
+    traffic = measured_traffic(nbytes)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "full latent 62x48x84: B=1, T=249984, H=16, D=64, fp16 fused QKV [1,249984,3072] "
+                               "-> Q fp32, K/V fp16 head-major [1,16,249984,64]",
+                   "global_batch": wl.B, "seq_len": wl.T, "parallelism": "none (one GPU)"},
+        "tokens_per_ms": round(tokens / r["ms_per_step"], 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "qk_kernel<D=64, f16 -> f32/f16, store>", "bytes_per_launch": nbytes,
+                     "kernel_us": round(r["kernel_ms"] * 1e3, 2)},
+    }
+    if args.extra:
+        extra = {}
+        for name, rot in (("tile", 8), ("tiles8", 1)):
+            w = synth.workloads()[name]
+            _, rr = bench_store(w, max(10, args.steps // 2), args.warmup, rotate=rot)
+            extra[name] = {"kernel_us": round(rr["kernel_ms"] * 1e3, 2),
+                           "GBs": round(rr["bytes"] / rr["kernel_ms"] / 1e6, 1),
+                           "frac_of_peak": round(rr["bytes"] / rr["kernel_ms"] / 1e6 / HBM_PEAK_GBS, 4),
+                           "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
+                           "buffer_sets_rotated": rot}
+        extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
+        out["extra"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pb)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * libh3qk — MiniMax-H3 attention input preparation on AMD MI355X (gfx950).
+ *
+ * One memory-bound pass over the fused QKV projection of a MiniMax-H3 attention block:
+ * per-head RMS normalisation of every Q and K head row with a learned per-dim weight, partial
+ * 3-axis (t, h, w) rotary embedding, and a head-major store of Q, K and V; plus an FP8 variant
+ * (per-tensor amax pass, then a cast pass to OCP E4M3FN codes with descales).
+ *
+ * Pages the operations follow:
+ *   [SDCPP-19]  stable-diffusion.cpp PR #19 "MiniMax-H3: sage takes the fused RoPE op, faster
+ *               video and audio VAE decode": commit messages on the fused QKV decoder path
+ *               (q/k normalised on the fused projection, partial RoPE, F32 Q and F16 K/V written
+ *               head-major) and on ggml_rope_pe_permute_rms (norm fused into the RoPE/permute op).
+ *   [OMNI-6607] vllm-omni PR #6607 (MiniMax-H3 video VAE decoder eager ops), "Operations" table:
+ *               one fused reduction + RoPE per Q/K tensor with a fixed RMS reduction tree and
+ *               explicit rounding, bitwise equal to its reference; scaled residual and SwiGLU rows.
+ *   [TRT-21485] TensorRT-LLM PR #21485 "cuDNN FP8 attention path for MiniMax-H3 on SM107 under
+ *               Ulysses": Summary (QK-norm, RoPE and the per-tensor FP8 cast fused into one amax
+ *               pass and one cast pass), commit messages on norm_rope_tensor(x, weight, cos, sin,
+ *               eps), the packed-QKV row stride, outputs that may not alias inputs, and the
+ *               per-item valid length that keeps padded rows out of the amax.
+ *
+ * Numerical contract (identical on every call, bitwise reproducible):
+ *   x_d  = the 16-bit input value, exactly, as binary32
+ *   a_d  = x_d * x_d                                  (binary32, round to nearest even)
+ *   fixed halving tree: for o = D/2, D/4, ..., 1 and d < o: a_d = a_d + a_{d+o}; ss = a_0
+ *   r    = 1 / sqrt(ss * (1/D) + eps)                 (correctly rounded sqrt, then division)
+ *   y_d  = (x_d * r) * w_d
+ *   pair p < 3n (n = pairs_per_axis): axis = p / n (0 = t, 1 = h, 2 = w), j = p mod n,
+ *     (c, s) = (cos_tab, sin_tab)[base_axis + pos_axis][j], base = (0, P_t, P_t + P_h);
+ *     y'_{2p} = e*c - f*s,  y'_{2p+1} = e*s + f*c      (e = y_{2p}, f = y_{2p+1}; each product
+ *     rounded, then the sum); dims >= 6n pass through.
+ * No fused multiply-add anywhere in this chain, IEEE denormals, round to nearest even at every
+ * store.  Token i of item b sits at grid position (i / (Gh*Gw), (i / Gw) mod Gh, i mod Gw) plus
+ * pos_offset[b]; tokens i >= valid_len[b] are padding: all their outputs are +0 (code 0x00) and
+ * they never enter the amax.
+ *
+ * Conventions for every entry point:
+ *   - data pointers are DEVICE pointers (HIP global memory) unless marked HOST; the descriptor
+ *     itself is a HOST struct read during the call only;
+ *   - work is enqueued on `stream` (0 = the null stream) and is asynchronous: no host sync;
+ *   - the caller owns every buffer; the library allocates no device or host memory and keeps no
+ *     pointer after it returns;
+ *   - arguments are validated on the host before anything is enqueued: a call that returns an
+ *     error has enqueued nothing (all or nothing), and h3_last_error() describes the failure;
+ *   - the unsupported cases return H3_EUNSUPPORTED so a caller can keep its own path;
+ *   - outputs must not overlap any input or any other output (H3_EALIAS).
+ */
+#ifndef H3QK_H
+#define H3QK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3_ABI_VERSION 1
+#define H3_MAX_BATCH 64
+
+typedef enum { H3_F32 = 0, H3_F16 = 1, H3_BF16 = 2, H3_E4M3FN = 3 } h3_dtype;
+
+enum {
+    H3_OK = 0,
+    H3_EINVAL = -1,       /* null pointer, non-positive size, bad stride or eps */
+    H3_EUNSUPPORTED = -2, /* head dim, dtype combination or rotary split not provided */
+    H3_EALIGN = -3,       /* a pointer or stride is not 16-byte aligned */
+    H3_ERANGE = -4,       /* valid_len or a position falls outside the grid or the tables */
+    H3_EALIAS = -5,       /* an output overlaps an input or another output */
+    H3_ELAUNCH = -6       /* the HIP runtime refused the launch (message in h3_last_error) */
+};
+
+/* Problem description shared by the three QK entry points (a HOST struct). */
+typedef struct {
+    int32_t B;                 /* items in the batch, 1..H3_MAX_BATCH */
+    int32_t T;                 /* padded tokens per item (>= 1) */
+    int32_t H;                 /* heads (>= 1) */
+    int32_t D;                 /* head dim: 64 or 128 */
+    int64_t row_stride;        /* elements between consecutive tokens of the fused projection,
+                                  >= 3*H*D, multiple of 8 (16 bytes) */
+    int64_t batch_stride;      /* elements between consecutive items, multiple of 8,
+                                  >= T*row_stride when B > 1 */
+    int32_t grid[3];           /* Gt, Gh, Gw: token i -> (i/(Gh*Gw), (i/Gw)%Gh, i%Gw) */
+    int32_t pos_offset[H3_MAX_BATCH][3]; /* per-item (t, h, w) position offsets, >= 0 */
+    int32_t valid_len[H3_MAX_BATCH];     /* per-item valid tokens, 0..min(T, Gt*Gh*Gw) */
+    int32_t pairs_per_axis;    /* n: rotated pairs per axis, 0 <= 6n <= D */
+    int32_t table_len[3];      /* P_t, P_h, P_w: rows of the t, h, w parts of the tables;
+                                  pos_offset[b][a] + grid[a] <= table_len[a] for every item */
+    const float *cos_tab;      /* DEVICE fp32 [(P_t + P_h + P_w)][n], axis-major t, h, w;
+                                  never read (may be NULL) when n = 0 */
+    const float *sin_tab;      /* DEVICE fp32, same layout */
+    float eps;                 /* finite, >= 0 */
+} h3_qk_desc;
+
+/*
+ * Fused RMSNorm + partial 3-axis RoPE + head-major permute, one pass.
+ *   qkv    DEVICE, in_dt (H3_F16 or H3_BF16), item b token i at qkv + b*batch_stride +
+ *          i*row_stride, laid out [Q heads | K heads | V heads], each head's D values contiguous
+ *   w_q, w_k  DEVICE fp32 [D] norm weights (shared by all heads)
+ *   q_out  DEVICE [B, H, T, D] contiguous, q_dt in {H3_F32, H3_F16, H3_BF16}
+ *   k_out  DEVICE [B, H, T, D] contiguous, k_dt in {H3_F32, H3_F16, H3_BF16}
+ *   v_out  DEVICE [B, H, T, D] contiguous, dtype in_dt: a bit copy of the V heads
+ * Q and K take y' rounded (RNE) to their dtypes; padding tokens are written as +0.
+ * Follows [SDCPP-19] (fused QKV path, ggml_rope_pe_permute_rms) and [OMNI-6607] (Q/K
+ * normalization + RoPE row).
+ */
+int h3_qk_rmsnorm_rope_permute(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                               const float *w_q, const float *w_k,
+                               void *q_out, h3_dtype q_dt, void *k_out, h3_dtype k_dt,
+                               void *v_out, hipStream_t stream);
+
+/*
+ * FP8 amax pass: amax_qk[0] = max |y'| over the valid Q rows of all items, amax_qk[1] the same
+ * over the valid K rows ([TRT-21485] Summary and valid-length commit).
+ *   amax_qk  DEVICE fp32 [2], overwritten (cleared on the stream, then reduced into).
+ * Max is exact, so the result does not depend on the reduction order.  A NaN y' makes the
+ * result NaN.  A multi-GPU caller all-reduces (MAX) amax_qk between this call and the cast.
+ */
+int h3_qk_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+               const float *w_q, const float *w_k, float *amax_qk, hipStream_t stream);
+
+/*
+ * FP8 cast pass ([TRT-21485] Summary and fused_fp8_qk commit):
+ *   descale_s = amax_qk[s] / 448 if amax_qk[s] > 0, else 1   (read on the device, no host sync)
+ *   q_codes / k_codes  DEVICE uint8 [B, H, T, D]: E4M3FN(y' / descale_s), round to nearest
+ *                      even, saturating to +-448; 0x00 for padding tokens
+ *   v_out              DEVICE [B, H, T, D], dtype in_dt: bit copy of the V heads (+0 for padding)
+ *   descale_qk         DEVICE fp32 [2] out: the two descales for the attention consumer
+ *   amax_qk            DEVICE fp32 [2] in (from h3_qk_amax, or 448 * a static descale)
+ */
+int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                    const float *w_q, const float *w_k, const float *amax_qk,
+                    uint8_t *q_codes, uint8_t *k_codes, void *v_out, float *descale_qk,
+                    hipStream_t stream);
+
+/* Thread-local text of the last error of an h3_* call on this thread ("" after success);
+   valid until the next h3_* call on the same thread. */
+const char *h3_last_error(void);
+
+/* H3_ABI_VERSION of the built library. */
+int h3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3QK_H */

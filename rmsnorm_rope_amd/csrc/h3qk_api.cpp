@@ -1,0 +1,225 @@
+// C ABI of libh3qk: host-side validation of every argument, then one launch on the caller's
+// stream.  A call that fails validation enqueues nothing.  See include/h3qk.h for the contract.
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "h3qk.h"
+#include "h3qk_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+    g_err = msg;
+    return code;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    const char *name;
+};
+
+bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int elem_size(int dt) { return dt == H3_F32 ? 4 : (dt == H3_E4M3FN ? 1 : 2); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate the descriptor and the input pointers shared by the three QK calls; fill the kernel
+// parameters.  Returns H3_OK or an error code with g_err set.
+int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q, const float *w_k,
+               h3::QkParams *p, std::vector<Range> *inputs) {
+    if (!d) return fail(H3_EINVAL, "desc is NULL");
+    if (!qkv || !w_q || !w_k) return fail(H3_EINVAL, "qkv, w_q and w_k must be non-NULL");
+    if (d->pairs_per_axis > 0 && (!d->cos_tab || !d->sin_tab))
+        return fail(H3_EINVAL, "cos_tab and sin_tab must be non-NULL when pairs_per_axis > 0");
+    if (d->B < 1 || d->B > H3_MAX_BATCH) return fail(H3_EINVAL, "B must be in 1..H3_MAX_BATCH");
+    if (d->T < 1 || d->H < 1) return fail(H3_EINVAL, "T and H must be >= 1");
+    if (d->D != 64 && d->D != 128) return fail(H3_EUNSUPPORTED, "head dim D must be 64 or 128");
+    if (in_dt != H3_F16 && in_dt != H3_BF16) return fail(H3_EUNSUPPORTED, "input dtype must be H3_F16 or H3_BF16");
+    const int64_t B = d->B, T = d->T, H = d->H, D = d->D;
+    if (d->pairs_per_axis < 0 || 6 * (int64_t)d->pairs_per_axis > D)
+        return fail(H3_EUNSUPPORTED, "pairs_per_axis n must satisfy 0 <= 6n <= D");
+    if (!std::isfinite(d->eps) || d->eps < 0.0f) return fail(H3_EINVAL, "eps must be finite and >= 0");
+    if (d->row_stride < 3 * H * D) return fail(H3_EINVAL, "row_stride must be >= 3*H*D");
+    if (B > 1 && d->batch_stride < T * d->row_stride) return fail(H3_EINVAL, "batch_stride must be >= T*row_stride");
+    if (d->batch_stride < 0) return fail(H3_EINVAL, "batch_stride must be >= 0");
+    if ((d->row_stride & 7) || (d->batch_stride & 7))
+        return fail(H3_EALIGN, "row_stride and batch_stride must be multiples of 8 elements (16 bytes)");
+    if (!aligned16(qkv) || !aligned16(w_q) || !aligned16(w_k))
+        return fail(H3_EALIGN, "qkv, w_q and w_k must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(d->cos_tab) & 3u) || (reinterpret_cast<uintptr_t>(d->sin_tab) & 3u))
+        return fail(H3_EALIGN, "cos_tab and sin_tab must be 4-byte aligned");
+    for (int a = 0; a < 3; ++a) {
+        if (d->grid[a] < 1) return fail(H3_EINVAL, "grid extents must be >= 1");
+        if (d->table_len[a] < 1) return fail(H3_EINVAL, "table_len entries must be >= 1");
+    }
+    const int64_t gsize = (int64_t)d->grid[0] * d->grid[1] * d->grid[2];
+    const int64_t vmax = gsize < T ? gsize : T;
+    for (int b = 0; b < d->B; ++b) {
+        if (d->valid_len[b] < 0 || d->valid_len[b] > vmax)
+            return fail(H3_ERANGE, "valid_len[" + std::to_string(b) + "] must be in 0..min(T, Gt*Gh*Gw)");
+        for (int a = 0; a < 3; ++a) {
+            const int64_t off = d->pos_offset[b][a];
+            if (off < 0 || off + d->grid[a] > d->table_len[a])
+                return fail(H3_ERANGE, "pos_offset[" + std::to_string(b) + "][" + std::to_string(a) +
+                                           "] + grid extent exceeds table_len");
+        }
+    }
+    const int64_t rows_total = (int64_t)d->table_len[0] + d->table_len[1] + d->table_len[2];
+    if (rows_total * (int64_t)d->pairs_per_axis > INT32_MAX || T * H * D > ((int64_t)1 << 40))
+        return fail(H3_EINVAL, "problem too large");
+
+    const uintptr_t q0 = reinterpret_cast<uintptr_t>(qkv);
+    const int64_t qkv_elems = (B - 1) * d->batch_stride + (T - 1) * d->row_stride + 3 * H * D;
+    inputs->push_back({q0, q0 + (uintptr_t)qkv_elems * 2, "qkv"});
+    inputs->push_back({reinterpret_cast<uintptr_t>(w_q), reinterpret_cast<uintptr_t>(w_q) + (uintptr_t)D * 4, "w_q"});
+    inputs->push_back({reinterpret_cast<uintptr_t>(w_k), reinterpret_cast<uintptr_t>(w_k) + (uintptr_t)D * 4, "w_k"});
+    const uintptr_t tab_bytes = (uintptr_t)(rows_total * d->pairs_per_axis) * 4;
+    inputs->push_back({reinterpret_cast<uintptr_t>(d->cos_tab), reinterpret_cast<uintptr_t>(d->cos_tab) + tab_bytes, "cos_tab"});
+    inputs->push_back({reinterpret_cast<uintptr_t>(d->sin_tab), reinterpret_cast<uintptr_t>(d->sin_tab) + tab_bytes, "sin_tab"});
+
+    memset(p, 0, sizeof(*p));
+    p->qkv = static_cast<const uint16_t *>(qkv);
+    p->wq = w_q;
+    p->wk = w_k;
+    p->cos_tab = d->cos_tab;
+    p->sin_tab = d->sin_tab;
+    p->row_stride = d->row_stride;
+    p->batch_stride = d->batch_stride;
+    p->B = d->B;
+    p->T = d->T;
+    p->H = d->H;
+    p->n = d->pairs_per_axis;
+    p->Gh = d->grid[1];
+    p->Gw = d->grid[2];
+    p->base_h = d->table_len[0];
+    p->base_w = d->table_len[0] + d->table_len[1];
+    p->eps = d->eps;
+    for (int b = 0; b < d->B; ++b) {
+        for (int a = 0; a < 3; ++a) p->off[b][a] = d->pos_offset[b][a];
+        p->vlen[b] = d->valid_len[b];
+    }
+    // Work items: 8 tokens x a chunk of heads.  Split heads across waves only when the token
+    // groups alone would leave the chip under-filled (256 CUs x 32 waves).
+    p->groups = (int32_t)((T + 7) / 8);
+    const int64_t tg = B * p->groups;
+    int64_t chunks = (8192 + tg - 1) / tg;
+    if (chunks < 1) chunks = 1;
+    if (chunks > H) chunks = H;
+    p->heads_per_chunk = (int32_t)((H + chunks - 1) / chunks);
+    p->head_chunks = (int32_t)((H + p->heads_per_chunk - 1) / p->heads_per_chunk);
+    p->items = tg * p->head_chunks;
+    return H3_OK;
+}
+
+int check_outputs(const std::vector<Range> &inputs, const std::vector<Range> &outputs) {
+    for (size_t i = 0; i < outputs.size(); ++i) {
+        if (!aligned16(reinterpret_cast<const void *>(outputs[i].lo)))
+            return fail(H3_EALIGN, std::string(outputs[i].name) + " must be 16-byte aligned");
+        for (const Range &in : inputs)
+            if (overlaps(outputs[i], in))
+                return fail(H3_EALIAS, std::string(outputs[i].name) + " overlaps input " + in.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlaps(outputs[i], outputs[j]))
+                return fail(H3_EALIAS, std::string(outputs[i].name) + " overlaps output " + outputs[j].name);
+    }
+    return H3_OK;
+}
+
+Range out_range(const void *p, int64_t n, int dt, const char *name) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + (uintptr_t)n * elem_size(dt), name};
+}
+
+int run(int mode, int D, int in_dt, int q_dt, int k_dt, h3::QkParams &p, hipStream_t stream) {
+    std::string err;
+    const int rc = h3::launch_qk(mode, D, in_dt, q_dt, k_dt, p, stream, &err);
+    if (rc != H3_OK) return fail(rc, err);
+    g_err.clear();
+    return H3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3_qk_rmsnorm_rope_permute(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                               const float *w_q, const float *w_k, void *q_out, h3_dtype q_dt,
+                               void *k_out, h3_dtype k_dt, void *v_out, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!q_out || !k_out || !v_out) return fail(H3_EINVAL, "q_out, k_out and v_out must be non-NULL");
+    if (q_dt != H3_F32 && q_dt != H3_F16 && q_dt != H3_BF16)
+        return fail(H3_EUNSUPPORTED, "q_dt must be H3_F32, H3_F16 or H3_BF16");
+    if (k_dt != H3_F32 && k_dt != H3_F16 && k_dt != H3_BF16)
+        return fail(H3_EUNSUPPORTED, "k_dt must be H3_F32, H3_F16 or H3_BF16");
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    rc = check_outputs(inputs, {out_range(q_out, n, q_dt, "q_out"), out_range(k_out, n, k_dt, "k_out"),
+                                out_range(v_out, n, in_dt, "v_out")});
+    if (rc) return rc;
+    p.q = q_out;
+    p.k = k_out;
+    p.v = v_out;
+    return run(h3::MODE_STORE, desc->D, in_dt, q_dt, k_dt, p, stream);
+}
+
+int h3_qk_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+               const float *w_k, float *amax_qk, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!amax_qk) return fail(H3_EINVAL, "amax_qk must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(amax_qk) & 7u) return fail(H3_EALIGN, "amax_qk must be 8-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(amax_qk);
+    for (const Range &in : inputs)
+        if (overlaps({a, a + 8, "amax_qk"}, in)) return fail(H3_EALIAS, std::string("amax_qk overlaps input ") + in.name);
+    p.amax = amax_qk;
+    return run(h3::MODE_AMAX, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
+int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                    const float *w_k, const float *amax_qk, uint8_t *q_codes, uint8_t *k_codes,
+                    void *v_out, float *descale_qk, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!amax_qk || !q_codes || !k_codes || !v_out || !descale_qk)
+        return fail(H3_EINVAL, "amax_qk, q_codes, k_codes, v_out and descale_qk must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(amax_qk) & 7u) || (reinterpret_cast<uintptr_t>(descale_qk) & 7u))
+        return fail(H3_EALIGN, "amax_qk and descale_qk must be 8-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(amax_qk);
+    inputs.push_back({a, a + 8, "amax_qk"});
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    const uintptr_t ds = reinterpret_cast<uintptr_t>(descale_qk);
+    std::vector<Range> outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
+                               out_range(v_out, n, in_dt, "v_out")};
+    rc = check_outputs(inputs, outs);
+    if (rc) return rc;
+    const Range dr = {ds, ds + 8, "descale_qk"};
+    for (const Range &r : inputs)
+        if (overlaps(dr, r)) return fail(H3_EALIAS, std::string("descale_qk overlaps input ") + r.name);
+    for (const Range &r : outs)
+        if (overlaps(dr, r)) return fail(H3_EALIAS, std::string("descale_qk overlaps output ") + r.name);
+    p.amax = const_cast<float *>(amax_qk);
+    p.q = q_codes;
+    p.k = k_codes;
+    p.v = v_out;
+    p.descale = descale_qk;
+    return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
+const char *h3_last_error(void) { return g_err.c_str(); }
+
+int h3_abi_version(void) { return H3_ABI_VERSION; }
+
+}  // extern "C"

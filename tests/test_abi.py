@@ -1,0 +1,132 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every symbol include/h3qk.h
+declares, and validates arguments on the host before any HIP call (no compute call is made:
+every case here fails validation, so nothing reaches the runtime)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import rmsnorm_rope_amd as h3
+from rmsnorm_rope_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if _build.stale():
+        _build.build()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "h3qk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(h3_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(h3.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", h3.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (h3_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(h3.lib(), n)
+
+
+def test_abi_version():
+    assert h3.h3_abi_version() == 1
+
+
+# fake, well-aligned device addresses: validation never dereferences them
+BASE = 0x7F0000000000
+
+
+def desc(**kw):
+    a = dict(B=1, T=32, H=2, D=64, grid=(2, 4, 4), pairs_per_axis=8, table_len=(2, 4, 4),
+             cos_tab=BASE + 0x10000000, sin_tab=BASE + 0x11000000)
+    a.update(kw)
+    return h3.make_desc(**a)
+
+
+def call(d=None, qkv=BASE, in_dt=h3.F16, wq=BASE + 0x20000000, wk=BASE + 0x21000000,
+         q=BASE + 0x30000000, q_dt=h3.F32, k=BASE + 0x40000000, k_dt=h3.F16, v=BASE + 0x50000000):
+    d = desc() if d is None else d
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_rmsnorm_rope_permute(d, qkv, in_dt, wq, wk, q, q_dt, k, k_dt, v, stream=0)
+    return e.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), "H3_EINVAL"), (dict(B=65), "H3_EINVAL"), (dict(T=0), "H3_EINVAL"), (dict(H=0), "H3_EINVAL"),
+    (dict(D=96), "H3_EUNSUPPORTED"), (dict(D=256), "H3_EUNSUPPORTED"),
+    (dict(pairs_per_axis=11), "H3_EUNSUPPORTED"), (dict(pairs_per_axis=-1), "H3_EUNSUPPORTED"),
+    (dict(eps=float("nan")), "H3_EINVAL"), (dict(eps=-1.0), "H3_EINVAL"),
+    (dict(row_stride=3 * 2 * 64 - 8), "H3_EINVAL"), (dict(row_stride=3 * 2 * 64 + 4), "H3_EALIGN"),
+    (dict(B=2, batch_stride=32 * 384 - 8), "H3_EINVAL"),
+    (dict(grid=(0, 4, 4)), "H3_EINVAL"), (dict(table_len=(2, 4, 3)), "H3_ERANGE"),
+    (dict(valid_len=[33]), "H3_ERANGE"), (dict(valid_len=[-1]), "H3_ERANGE"),
+    (dict(T=40, valid_len=[33]), "H3_ERANGE"),             # more valid tokens than grid positions
+    (dict(pos_offset=[[1, 0, 0]]), "H3_ERANGE"), (dict(pos_offset=[[0, -1, 0]]), "H3_ERANGE"),
+    (dict(cos_tab=0), "H3_EINVAL"), (dict(sin_tab=BASE + 2), "H3_EALIGN"),
+])
+def test_descriptor_validation(kw, code):
+    assert call(desc(**kw)).name == code
+
+
+def test_pointer_validation():
+    assert call(qkv=0).name == "H3_EINVAL"
+    assert call(q=0).name == "H3_EINVAL"
+    assert call(qkv=BASE + 8).name == "H3_EALIGN"
+    assert call(wq=BASE + 0x20000004).name == "H3_EALIGN"
+    assert call(q=BASE + 0x30000008).name == "H3_EALIGN"
+    assert call(in_dt=h3.F32).name == "H3_EUNSUPPORTED"
+    assert call(q_dt=h3.E4M3FN).name == "H3_EUNSUPPORTED"
+    assert call(k_dt=7).name == "H3_EUNSUPPORTED"
+
+
+def test_alias_validation():
+    # q_out inside the input
+    assert call(q=BASE + 4096).name == "H3_EALIAS"
+    # k_out overlapping q_out (q is 32*2*64*4 = 16 KiB)
+    assert call(k=BASE + 0x30000000 + 8192).name == "H3_EALIAS"
+    # v_out on a weight
+    assert call(v=BASE + 0x20000000).name == "H3_EALIAS"
+    # outputs adjacent but not overlapping are fine up to validation (checked via amax path below)
+    e = call(q=BASE + 0x30000000, k=BASE + 0x30000000 + 16384 - 16)
+    assert e.name == "H3_EALIAS"
+    msg = h3.h3_last_error()
+    assert "k_out" in msg and "q_out" in msg
+
+
+def test_amax_and_cast_validation():
+    d = desc(D=128, pairs_per_axis=16)
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_amax(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, 0, stream=0)
+    assert e.value.name == "H3_EINVAL"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_amax(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 64, stream=0)
+    assert e.value.name == "H3_EALIAS"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_cast_e4m3(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x60000000,
+                           BASE + 0x30000000, BASE + 0x30000000 + 128, BASE + 0x50000000, BASE + 0x61000000,
+                           stream=0)
+    assert e.value.name == "H3_EALIAS"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_cast_e4m3(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x60000000,
+                           BASE + 0x30000000, BASE + 0x40000000, BASE + 0x50000000, BASE + 0x60000000,
+                           stream=0)
+    assert e.value.name == "H3_EALIAS"  # descale on top of amax
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_cast_e4m3(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x60000000,
+                           BASE + 0x30000000, BASE + 0x40000000, BASE + 0x50000000, BASE + 0x61000004,
+                           stream=0)
+    assert e.value.name == "H3_EALIGN"
+
+
+def test_null_descriptor():
+    rc = h3.lib().h3_qk_rmsnorm_rope_permute(None, BASE, 1, BASE, BASE, BASE, 0, BASE, 1, BASE, None)
+    assert rc == -1 and "desc" in h3.h3_last_error()
