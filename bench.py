@@ -135,6 +135,61 @@ def bench_fp8(wl, steps, warmup):
             "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1)}
 
 
+def pmc_summary(root):
+    """Write profiles/traffic_latent.txt from four rocprofv3 --pmc runs under `root`:
+    pmc_FETCH_SIZE, pmc_WRITE_SIZE (this bench) and pmccopy_FETCH_SIZE, pmccopy_WRITE_SIZE
+    (--copy-calibration).  Counters are KiB per dispatch; each is scaled by the ratio of the
+    copy's known bytes to what the same counter read for the copy."""
+    import csv
+    import glob
+
+    def per_dispatch(d, key):
+        vals = []
+        for f in glob.glob(os.path.join(root, d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if key in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+        assert vals, (d, key)
+        return sum(vals) / len(vals), len(vals)
+
+    kern = "qk_kernel<64, 1, 0, 1, 0>"
+    fk, nf = per_dispatch("pmc_FETCH_SIZE", kern)
+    wk, nw = per_dispatch("pmc_WRITE_SIZE", kern)
+    cf, _ = per_dispatch("pmccopy_FETCH_SIZE", "copyBuffer")
+    cw, _ = per_dispatch("pmccopy_WRITE_SIZE", "copyBuffer")
+    copy_kib = (1 << 31) / 1024.0
+    fs, ws = copy_kib / cf, copy_kib / cw
+    rd, wr = fk * fs * 1024, wk * ws * 1024
+    lines = [
+        "# HBM traffic of the fused store kernel on the full-latent workload, from rocprofv3 --pmc.",
+        "# Commands (repository root R, run from /tmp with TMPDIR=/tmp), one counter per run:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE -o run --output-format csv -- "
+        "python3 $R/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE -o run --output-format csv -- "
+        "python3 $R/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+        "#   the same two with -d .../pmccopy_<counter> -- python3 $R/bench.py --copy-calibration "
+        "(a 2 GiB device copy: 2 GiB read, 2 GiB written)",
+        "#   python3 bench.py --pmc-summary $R/gpurun_out",
+        f"kernel_sha256_16={kernel_digest()}",
+        f"dispatches_fetch={nf}",
+        f"dispatches_write={nw}",
+        f"fetch_kib_per_dispatch={fk:.1f}",
+        f"write_kib_per_dispatch={wk:.1f}",
+        f"copy_fetch_kib={cf:.1f}",
+        f"copy_write_kib={cw:.1f}",
+        f"fetch_scale={fs:.5f}",
+        f"write_scale={ws:.5f}",
+        f"hbm_read_bytes_per_launch={rd:.0f}",
+        f"hbm_write_bytes_per_launch={wr:.0f}",
+        f"hbm_bytes_per_launch={rd + wr:.0f}",
+        "algorithmic_bytes_per_launch=3583770624",
+        f"traffic_over_algorithmic={(rd + wr) / 3583770624:.5f}",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_calibration(nbytes=1 << 31, steps=10):
     """A plain device copy of known size (torch's copy kernel), for scaling the PMC byte counters."""
     import torch
@@ -155,7 +210,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time the tile, eight-tile and FP8 workloads")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", metavar="DIR", help="write the traffic summary from rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (one process, one MI355X); "
               "--gpus must be 1", file=sys.stderr)

@@ -105,16 +105,14 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
         for (int a = 0; a < 3; ++a) p->off[b][a] = d->pos_offset[b][a];
         p->vlen[b] = d->valid_len[b];
     }
-    // Work items: 8 tokens x a chunk of heads.  Split heads across waves only when the token
-    // groups alone would leave the chip under-filled (256 CUs x 32 waves).
+    // Work items: 8 consecutive tokens x kHeadsPerWave heads, one wave each.
     p->groups = (int32_t)((T + 7) / 8);
-    const int64_t tg = B * p->groups;
-    int64_t chunks = (8192 + tg - 1) / tg;
-    if (chunks < 1) chunks = 1;
-    if (chunks > H) chunks = H;
-    p->heads_per_chunk = (int32_t)((H + chunks - 1) / chunks);
-    p->head_chunks = (int32_t)((H + p->heads_per_chunk - 1) / p->heads_per_chunk);
-    p->items = tg * p->head_chunks;
+    p->head_chunks = (int32_t)((H + h3::kHeadsPerWave - 1) / h3::kHeadsPerWave);
+    p->items = B * p->groups * p->head_chunks;
+    if (p->items > INT32_MAX) return fail(H3_EINVAL, "problem too large");
+    p->div_gw = h3::div_magic((uint32_t)d->grid[2]);
+    p->div_gh = h3::div_magic((uint32_t)d->grid[1]);
+    p->inv_n = d->pairs_per_axis > 0 ? 1.0f / (float)d->pairs_per_axis : 0.0f;
     return H3_OK;
 }
 

@@ -3,13 +3,50 @@
 #pragma once
 
 #include <stdint.h>
+
+#ifdef __HIPCC__
+#define H3_HD __host__ __device__
+#else
+#define H3_HD
+#endif
+
+#ifndef H3QK_NO_HIP
 #include <string>
 
 #include "h3qk.h"
+#endif
 
 namespace h3 {
 
+// Unsigned division of any 32-bit n by an invariant divisor d >= 1 with one multiply-high
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", PLDI 1994,
+// unsigned case): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+//   t = mulhi(m, n),  n / d = (t + ((n - t) >> s1)) >> s2,  s1 = min(l, 1), s2 = max(l - 1, 0).
+struct DivMagic {
+    uint32_t m, s1, s2, d;
+};
+
+inline DivMagic div_magic(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    DivMagic r;
+    r.m = (uint32_t)m;
+    r.s1 = l ? 1u : 0u;
+    r.s2 = l ? l - 1u : 0u;
+    r.d = d;
+    return r;
+}
+
+H3_HD inline uint32_t div_apply(uint32_t n, const DivMagic &g) {
+    const uint32_t t = (uint32_t)(((uint64_t)g.m * n) >> 32);
+    return (t + ((n - t) >> g.s1)) >> g.s2;
+}
+
+#ifndef H3QK_NO_HIP
 enum Mode : int { MODE_STORE = 0, MODE_AMAX = 1, MODE_CAST = 2 };
+
+constexpr int kHeadsPerWave = 2;  // heads of one 8-token group served by one wave
 
 // Everything a QK kernel reads, passed by value in the kernel arguments (< 1.5 KiB).
 struct QkParams {
@@ -25,15 +62,15 @@ struct QkParams {
     float *descale;     // MODE_CAST: written by the first wave
     int64_t row_stride;
     int64_t batch_stride;
+    int64_t items;               // B * groups * head_chunks
     int32_t B, T, H, n;
     int32_t Gh, Gw;
     int32_t base_h, base_w;      // first table row of the h and w parts
     int32_t groups;              // token groups of 8 per item: ceil(T / 8)
-    int32_t head_chunks;         // work items per token group (heads split across waves)
-    int32_t heads_per_chunk;
-    int32_t pad_;
-    int64_t items;               // B * groups * head_chunks
+    int32_t head_chunks;         // ceil(H / kHeadsPerWave)
+    DivMagic div_gw, div_gh;     // token -> (t, h, w) decode
     float eps;
+    float inv_n;                 // 1 / n (pair -> axis decode), 0 when n = 0
     int32_t off[H3_MAX_BATCH][3];
     int32_t vlen[H3_MAX_BATCH];
 };
@@ -41,5 +78,6 @@ struct QkParams {
 // Launch one QK pass.  Returns H3_OK or H3_ELAUNCH / H3_EUNSUPPORTED with *err filled.
 int launch_qk(int mode, int D, int in_dt, int q_dt, int k_dt, QkParams &p, hipStream_t stream,
               std::string *err);
+#endif
 
 }  // namespace h3

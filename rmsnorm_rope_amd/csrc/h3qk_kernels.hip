@@ -4,20 +4,28 @@
 // fused_fp8_qk commits).  The numerical contract is stated in include/h3qk.h.
 //
 // Work decomposition (wave64):
-//   * A work item is 8 consecutive tokens of one item and a chunk of its heads.  Lane
-//     l = 8 g + c serves token g of the 8 and holds, of every head row it touches, the dims
-//     {8W m + W c + k : m < M, k < W} with W = 4, M = 2 for D = 64 and W = 8, M = 2 for D = 128.
-//     Loads are then 8 W contiguous bytes per token per instruction, and the f32 Q store of a
-//     D = 64 row is two full 128-byte lines.
+//   * A work item is 8 consecutive tokens of one item and 2 of its heads.  Lane 8 g + l serves
+//     token g of the 8 and holds, of every head row it touches, the dims
+//     {8W m + W c + k : m < M, k < W} of its chunk c = chunk_of_lane(l), with W = 4, M = 2 for
+//     D = 64 and W = 8, M = 2 for D = 128.  Loads are 8 W contiguous bytes per token per instruction, the f32 Q store of a
+//     D = 64 row is two full 128-byte lines, V moves in 16-byte lanes.
 //   * The halving reduction tree maps onto that layout as: levels o >= 8W fold chunks inside
-//     the lane, levels 4W, 2W, W are cross-lane butterflies (lane c with c^4, c^2, c^1, the
-//     8 lanes of a token), levels below W fold inside the chunk.  Floating-point addition is
+//     the lane, levels 4W, 2W, W are DPP butterflies across the token's 8 lanes (half-mirror,
+//     then xor 2, then xor 1), levels below W fold inside the chunk.  Floating-point addition is
 //     commutative, so the butterfly partner computes the same bits as the tree node, and all
 //     8 lanes end with ss.
-//   * Each lane's rotary pairs depend only on its lane index, so their (axis, frequency) is
-//     computed once; the cos/sin entries of a token are loaded once and reused for every head.
-//   * Work items are taken grid-stride, so per-lane setup (weights, pair map) is paid once per
-//     wave, and the amax pass issues one atomic per wave and tensor.
+//   * Store and cast passes: one work item per wave, one short-lived 4-wave block per 8 tokens
+//     x 8 heads.  Blocks are dispatched in order, so the chip writes a narrow sliding window of
+//     each head plane of the [B, H, T, D] outputs; on MI355X that keeps HBM write efficiency
+//     well above a persistent grid-stride sweep, which holds a window of every plane open.
+//     Each wave issues its data loads first, then decodes positions and fetches weights and
+//     rotary entries while the loads are in flight.  Outputs are written once and never read
+//     back, so they bypass the caches (nontemporal stores), each row as whole 128-byte lines.
+//     At most 3 blocks are resident per CU (see kStoreBlocksPerCU).
+//   * Amax pass: persistent waves over the work items with the next item's loads in flight
+//     while the current one is reduced, one atomic max per block and tensor.  It stores nothing,
+//     so it always takes W = 4 (M = D / 32), which keeps the cross-lane tree levels at 12 DPP adds
+//     per row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,6 +35,10 @@ namespace h3 {
 namespace {
 
 constexpr int DT_F32 = H3_F32, DT_F16 = H3_F16, DT_BF16 = H3_BF16, DT_E4M3 = H3_E4M3FN;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ element conversions
 
@@ -71,6 +83,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
     return code | sign;
 }
 
+// Four E4M3FN codes packed little-endian, by the gfx950 conversion instruction (round to nearest
+// even).  The instruction itself turns magnitudes from 464 up into NaN, so values are first
+// clamped to +-448 (NaN stays NaN: both comparisons are false).  For every non-NaN binary32 this
+// equals f32_to_e4m3; a NaN gives a NaN code whose sign bit is not specified.
+__device__ __forceinline__ float clamp448(float x) { return x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+    return (uint32_t)w;
+}
+
 template <int OT>
 __device__ __forceinline__ uint32_t encode_out(float x) {
     if constexpr (OT == DT_F16) return f32_to_f16_bits(x);
@@ -80,15 +103,23 @@ __device__ __forceinline__ uint32_t encode_out(float x) {
 
 // ------------------------------------------------------------------ cross-lane butterflies
 
+// Every source lane of these patterns exists, so bound_ctrl never applies; setting it lets the
+// compiler fold the move into the consuming add (v_add_f32 with a DPP source).
 __device__ __forceinline__ float lane_xor1(float v) {  // DPP quad_perm [1,0,3,2]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float lane_xor2(float v) {  // DPP quad_perm [2,3,0,1]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float lane_xor4(float v) {  // ds_swizzle bit mode: and 0x1F, xor 4
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+__device__ __forceinline__ float lane_mirror8(float v) {  // DPP row_half_mirror: lane l <-> 7 - l
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
 }
+
+// Chunk held by lane l of a token's 8 lanes: l for l < 4, 11 - l for l >= 4.  Chunk ch + 4 then
+// sits in the half-mirror lane 7 - ch, so the first cross-lane tree level pairs mirror lanes and
+// the next two pair lanes l ^ 2 and l ^ 1 (lane l >= 4 stands for node 7 - l = l ^ 7, whose
+// partners l ^ 7 ^ 2 and l ^ 7 ^ 1 live in lanes l ^ 2 and l ^ 1).  All three are DPP moves.
+__device__ __forceinline__ int chunk_of_lane(int l) { return l < 4 ? l : 11 - l; }
 
 // ------------------------------------------------------------------ loads and stores
 
@@ -96,52 +127,111 @@ __device__ __forceinline__ float lane_xor4(float v) {  // ds_swizzle bit mode: a
 template <int W>
 __device__ __forceinline__ void load_chunk(const uint16_t *p, uint32_t (&r)[W / 2]) {
     if constexpr (W == 4) {
-        uint2 t = *reinterpret_cast<const uint2 *>(p);
+        const u32x2 t = *reinterpret_cast<const u32x2 *>(p);
         r[0] = t.x; r[1] = t.y;
     } else {
-        uint4 t = *reinterpret_cast<const uint4 *>(p);
+        const u32x4 t = *reinterpret_cast<const u32x4 *>(p);
         r[0] = t.x; r[1] = t.y; r[2] = t.z; r[3] = t.w;
     }
 }
 
-// Store W values of one chunk in output dtype OT at element offset `e` of `base`.
+__device__ __forceinline__ void st_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(f32x4 *p, f32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// Store W encoded values of one chunk in output dtype OT at element offset `e` of `base`.
+template <int OT, int W>
+__device__ __forceinline__ void store_codes(void *base, int64_t e, const uint32_t (&w)[W]) {
+    if constexpr (OT == DT_E4M3) {
+        uint8_t *p = reinterpret_cast<uint8_t *>(base) + e;
+        uint32_t pk[W / 4];
+#pragma unroll
+        for (int k = 0; k < W; k += 4) pk[k / 4] = w[k] | (w[k + 1] << 8) | (w[k + 2] << 16) | (w[k + 3] << 24);
+        if constexpr (W == 4) st_nt(reinterpret_cast<uint32_t *>(p), pk[0]);
+        else st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){pk[0], pk[1]});
+    } else {
+        uint16_t *p = reinterpret_cast<uint16_t *>(base) + e;
+        uint32_t pk[W / 2];
+#pragma unroll
+        for (int k = 0; k < W; k += 2) pk[k / 2] = w[k] | (w[k + 1] << 16);
+        if constexpr (W == 4) st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){pk[0], pk[1]});
+        else st_nt(reinterpret_cast<u32x4 *>(p), (u32x4){pk[0], pk[1], pk[2], pk[3]});
+    }
+}
+
 template <int OT, int W>
 __device__ __forceinline__ void store_chunk(void *base, int64_t e, const float (&y)[W]) {
     if constexpr (OT == DT_F32) {
         float *p = reinterpret_cast<float *>(base) + e;
 #pragma unroll
         for (int k = 0; k < W; k += 4)
-            *reinterpret_cast<float4 *>(p + k) = make_float4(y[k], y[k + 1], y[k + 2], y[k + 3]);
+            st_nt(reinterpret_cast<f32x4 *>(p + k), (f32x4){y[k], y[k + 1], y[k + 2], y[k + 3]});
     } else if constexpr (OT == DT_E4M3) {
         uint8_t *p = reinterpret_cast<uint8_t *>(base) + e;
-        uint32_t w[W / 4];
-#pragma unroll
-        for (int k = 0; k < W; k += 4)
-            w[k / 4] = encode_out<OT>(y[k]) | (encode_out<OT>(y[k + 1]) << 8) |
-                       (encode_out<OT>(y[k + 2]) << 16) | (encode_out<OT>(y[k + 3]) << 24);
-        if constexpr (W == 4) *reinterpret_cast<uint32_t *>(p) = w[0];
-        else *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+        if constexpr (W == 4) {
+            st_nt(reinterpret_cast<uint32_t *>(p), e4m3x4(y[0], y[1], y[2], y[3]));
+        } else {
+            st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7])});
+        }
     } else {
-        uint16_t *p = reinterpret_cast<uint16_t *>(base) + e;
-        uint32_t w[W / 2];
+        uint32_t w[W];
 #pragma unroll
-        for (int k = 0; k < W; k += 2) w[k / 2] = encode_out<OT>(y[k]) | (encode_out<OT>(y[k + 1]) << 16);
-        if constexpr (W == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
-        else *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int k = 0; k < W; ++k) w[k] = encode_out<OT>(y[k]);
+        store_codes<OT, W>(base, e, w);
     }
 }
 
 template <int OT, int W>
 __device__ __forceinline__ void store_zero_chunk(void *base, int64_t e) {
-    float z[W];
+    if constexpr (OT == DT_F32) {
+        float *p = reinterpret_cast<float *>(base) + e;
 #pragma unroll
-    for (int k = 0; k < W; ++k) z[k] = 0.0f;
-    store_chunk<OT, W>(base, e, z);
+        for (int k = 0; k < W; k += 4) st_nt(reinterpret_cast<f32x4 *>(p + k), (f32x4){0.f, 0.f, 0.f, 0.f});
+    } else {
+        uint32_t w[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) w[k] = 0u;
+        store_codes<OT, W>(base, e, w);
+    }
 }
+
+// Whole-row store of the lane's M = 2 chunks for 8-byte chunks (16-bit outputs with W = 4,
+// E4M3 with W = 8): neighbouring lanes (chunks 2j and 2j + 1, always lanes l and l ^ 1 under
+// chunk_of_lane) swap halves with one DPP move per word, so the even-chunk lane holds the 16 bytes
+// of chunks 2j, 2j + 1 of the first half-row and the odd one those of the second half-row.  One
+// 16-byte store per lane then writes the token's row as whole 128-byte lines, which reach HBM
+// without depending on the L2 to merge two half-line writes.
+template <int OT, int W>
+__device__ __forceinline__ void store_row_pairs(void *base, int64_t row_e, int c, const float (&y)[2][W]) {
+    static_assert((OT == DT_E4M3 && W == 8) || ((OT == DT_F16 || OT == DT_BF16) && W == 4), "8-byte chunks");
+    uint32_t m0[2], m1[2];
+    if constexpr (OT == DT_E4M3) {
+        m0[0] = e4m3x4(y[0][0], y[0][1], y[0][2], y[0][3]); m0[1] = e4m3x4(y[0][4], y[0][5], y[0][6], y[0][7]);
+        m1[0] = e4m3x4(y[1][0], y[1][1], y[1][2], y[1][3]); m1[1] = e4m3x4(y[1][4], y[1][5], y[1][6], y[1][7]);
+    } else {
+        m0[0] = encode_out<OT>(y[0][0]) | (encode_out<OT>(y[0][1]) << 16);
+        m0[1] = encode_out<OT>(y[0][2]) | (encode_out<OT>(y[0][3]) << 16);
+        m1[0] = encode_out<OT>(y[1][0]) | (encode_out<OT>(y[1][1]) << 16);
+        m1[1] = encode_out<OT>(y[1][2]) | (encode_out<OT>(y[1][3]) << 16);
+    }
+    const bool odd = c & 1;
+    const uint32_t s0 = odd ? m0[0] : m1[0], s1 = odd ? m0[1] : m1[1];
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xF, 0xF, true);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xF, 0xF, true);
+    const u32x4 v = odd ? (u32x4){r0, r1, m1[0], m1[1]} : (u32x4){m0[0], m0[1], r0, r1};
+    // even chunk 2j: elements [2j W, 2j W + 2W); odd chunk 2j + 1: [8W + 2j W, 8W + 2j W + 2W)
+    const int64_t e = row_e + (odd ? 8 * W + (c - 1) * W : c * W);
+    constexpr int EB = OT == DT_E4M3 ? 1 : 2;
+    st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(base) + e * EB), v);
+}
+
+template <int OT, int W, int M>
+constexpr bool kPairStore = M == 2 && ((OT == DT_E4M3 && W == 8) || ((OT == DT_F16 || OT == DT_BF16) && W == 4));
 
 // ------------------------------------------------------------------ the row
 
-// One Q or K head row held as x[m][k] (dim 8W m + W c + k of lane c): RMS normalisation with
+// One Q or K head row held as x[m][k] (dim 8W m + W ch + k, ch the lane's chunk): RMS normalisation with
 // weight w, then the rotation of the lane's pairs.  Binary32, one rounding per operation, the
 // halving reduction tree of the contract, no contraction (built with -ffp-contract=off).
 template <int W, int M>
@@ -161,9 +251,9 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[M][W], const float (&w)
         for (int m = 0; m < om; ++m)
 #pragma unroll
             for (int k = 0; k < W; ++k) a[m][k] = a[m][k] + a[m + om][k];
-    // levels 4W, 2W, W: lanes c and c + 4, c + 2, c + 1 of the token's 8 lanes
+    // levels 4W, 2W, W across the token's 8 lanes (see chunk_of_lane)
 #pragma unroll
-    for (int k = 0; k < W; ++k) a[0][k] = a[0][k] + lane_xor4(a[0][k]);
+    for (int k = 0; k < W; ++k) a[0][k] = a[0][k] + lane_mirror8(a[0][k]);
 #pragma unroll
     for (int k = 0; k < W; ++k) a[0][k] = a[0][k] + lane_xor2(a[0][k]);
 #pragma unroll
@@ -197,187 +287,324 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[M][W], const float (&w)
         }
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+template <int W, int M, int IN>
+__device__ __forceinline__ void unpack_row(const uint32_t (&r)[M][W / 2], float (&x)[M][W]) {
 #pragma unroll
-    for (int o = 32; o >= 1; o /= 2) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) {
+            x[m][2 * k] = in_to_f32<IN>(r[m][k] & 0xFFFFu);
+            x[m][2 * k + 1] = in_to_f32<IN>(r[m][k] >> 16);
+        }
 }
 
-// ------------------------------------------------------------------ the kernel
+template <int W, int M>
+__device__ __forceinline__ void load_weights(const float *wsrc, int c, float (&w)[M][W]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W; k += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(wsrc + 8 * W * m + W * c + k);
+            w[m][k] = a.x; w[m][k + 1] = a.y; w[m][k + 2] = a.z; w[m][k + 3] = a.w;
+        }
+}
+
+// Rotary entries of this lane's pairs for token i of item b.  Pair index pr (the dims 2 pr,
+// 2 pr + 1) rotates when pr < 3n, on axis pr / n at frequency pr mod n; the axis comes from
+// floor((pr + 1/2) / n) in binary32, exact because pr + 1/2 is never a multiple of n and the
+// rounding error is far below the 1/(2n) margin for pr < 128.
+template <int W, int M>
+__device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, int c,
+                                               float (&cs)[M][W / 2], float (&sn)[M][W / 2],
+                                               bool (&rot)[M][W / 2]) {
+    const uint32_t ui = (uint32_t)i;
+    const uint32_t j = div_apply(ui, p.div_gw);   // i / Gw
+    const uint32_t tq = div_apply(j, p.div_gh);   // i / (Gh Gw)
+    const int row_t = (int)tq + p.off[b][0];
+    const int row_h = p.base_h + (int)(j - tq * (uint32_t)p.Gh) + p.off[b][1];
+    const int row_w = p.base_w + (int)(ui - j * (uint32_t)p.Gw) + p.off[b][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) {
+            const int pr = 4 * W * m + (W / 2) * c + q;
+            rot[m][q] = pr < 3 * p.n;
+            const int axis = (int)(((float)pr + 0.5f) * p.inv_n);
+            const int jj = pr - axis * p.n;
+            const int row = axis == 0 ? row_t : (axis == 1 ? row_h : row_w);
+            const int idx = row * p.n + jj;
+            cs[m][q] = rot[m][q] ? p.cos_tab[idx] : 1.0f;
+            sn[m][q] = rot[m][q] ? p.sin_tab[idx] : 0.0f;
+        }
+}
+
+// code of RN(y / ds) in E4M3FN.  Fast path: q0 = RN(y * rcp) with rcp = RN(1 / ds) is within
+// about 2 ulps of y / ds.  An E4M3 code only changes across the midpoints of the E4M3 grid,
+// which in the normal E4M3 range are the binary32 values whose 20 low significand bits are
+// 0x80000; when q0 is more than 4 ulps from such a midpoint and |q0| >= 2^-6, RN(y / ds) lies on
+// the same side of every midpoint and has the same code.  Otherwise (or when ds is outside the
+// normal range where rcp is exact enough) the quotient is computed by correctly rounded division.
+__device__ __forceinline__ float quotient_fast(float y, float rcp, bool *slow) {
+    const float q0 = y * rcp;
+    const uint32_t a = __float_as_uint(q0) & 0x7FFFFFFFu;
+    const int d = (int)(a & 0xFFFFFu) - 0x80000;
+    *slow = a < 0x3C800000u || (d <= 4 && d >= -4);
+    return q0;
+}
+
+// ------------------------------------------------------------------ store / cast kernel
 
 template <int D, int IN, int QT, int KT, int MODE>
 __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     constexpr int W = (D == 64) ? 4 : 8;
     constexpr int M = D / (8 * W);
     constexpr int VC = D / 64;  // 16-byte V chunks per lane
-    constexpr int U = (D == 64) ? 4 : 2;  // heads whose loads are in flight together
+    constexpr int HPW = kHeadsPerWave;
     static_assert(M >= 1 && 8 * W * M == D, "layout");
+    static_assert(MODE == MODE_STORE || MODE == MODE_CAST, "store / cast kernel");
 
     const int lane = threadIdx.x & 63;
-    const int c = lane & 7;
+    const int c = chunk_of_lane(lane & 7);  // chunk of the row this lane holds
     const int g = lane >> 3;
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const float inv_d = 1.0f / (float)D;
+    const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // pair map of this lane: chunk m, pair q -> (axis, frequency); fixed for the whole kernel
-    int paxis[M][W / 2], pj[M][W / 2];
-    bool rot[M][W / 2];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int q = 0; q < W / 2; ++q) {
-            const int pr = (8 * W * m + W * c + 2 * q) >> 1;
-            rot[m][q] = pr < 3 * p.n;
-            paxis[m][q] = rot[m][q] ? pr / p.n : 0;
-            pj[m][q] = rot[m][q] ? pr - paxis[m][q] * p.n : 0;
-        }
-    float wq[M][W], wk[M][W];
-    {
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int k = 0; k < W; k += 4) {
-                const float4 a = *reinterpret_cast<const float4 *>(p.wq + 8 * W * m + W * c + k);
-                const float4 b = *reinterpret_cast<const float4 *>(p.wk + 8 * W * m + W * c + k);
-                wq[m][k] = a.x; wq[m][k + 1] = a.y; wq[m][k + 2] = a.z; wq[m][k + 3] = a.w;
-                wk[m][k] = b.x; wk[m][k + 1] = b.y; wk[m][k + 2] = b.z; wk[m][k + 3] = b.w;
-            }
-    }
-    float ds[2] = {1.0f, 1.0f};
+    float ds[2] = {1.0f, 1.0f}, rcp[2] = {1.0f, 1.0f};
+    bool fast = false;
     if constexpr (MODE == MODE_CAST) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const float am = p.amax[s];
             ds[s] = am > 0.0f ? am / 448.0f : 1.0f;
+            rcp[s] = 1.0f / ds[s];
         }
-        if (wave0 == 0 && lane == 0) {
+        fast = ds[0] >= 0x1p-125f && ds[0] <= 0x1p125f && ds[1] >= 0x1p-125f && ds[1] <= 0x1p125f;
+        if (item == 0 && lane == 0) {
             p.descale[0] = ds[0];
             p.descale[1] = ds[1];
         }
     }
-    uint32_t mx[2] = {0u, 0u};  // MODE_AMAX: max of |y'| bits (NaN above +inf)
+    if (item >= p.items) return;
 
-    for (int64_t item = wave0; item < p.items; item += nwaves) {
-        const int hc = (int)(item % p.head_chunks);
-        const int64_t bgi = item / p.head_chunks;
-        const int tg = (int)(bgi % p.groups);
-        const int b = (int)(bgi / p.groups);
-        const int i = tg * 8 + g;
-        if (i >= p.T) continue;  // ragged tail: the token's 8 lanes skip together
-        const bool valid = i < p.vlen[b];
-        if (MODE == MODE_AMAX && !valid) continue;
-        const int h0 = hc * p.heads_per_chunk;
-        const int h1 = min(p.H, h0 + p.heads_per_chunk);
+    const uint32_t it32 = (uint32_t)item;  // items < 2^31 (checked on the host)
+    const uint32_t bgi = it32 / (uint32_t)p.head_chunks;
+    const int hc = (int)(it32 - bgi * (uint32_t)p.head_chunks);
+    const uint32_t b32 = bgi / (uint32_t)p.groups;
+    const int tg = (int)(bgi - b32 * (uint32_t)p.groups);
+    const int b = (int)b32;
+    const int i = tg * 8 + g;
+    if (i >= p.T) return;  // ragged tail: the token's 8 lanes leave together
+    const int h0 = hc * HPW;
+    const int nh = min(HPW, p.H - h0);
+    const int64_t plane = (int64_t)p.T * D;
+    const int64_t orow = (((int64_t)b * p.H + h0) * p.T + i) * D;  // element of (b, h0, i, 0)
 
-        float cs[M][W / 2], sn[M][W / 2];
-        if (valid) {
-            const int pt = i / (p.Gh * p.Gw) + p.off[b][0];
-            const int ph = (i / p.Gw) % p.Gh + p.off[b][1];
-            const int pw = i % p.Gw + p.off[b][2];
-            const int rowoff[3] = {pt * p.n, (p.base_h + ph) * p.n, (p.base_w + pw) * p.n};
+    if (i >= p.vlen[b]) {  // padding token: +0 everywhere
+#pragma unroll
+        for (int u = 0; u < HPW; ++u) {
+            if (u >= nh) break;
+            const int64_t o = orow + u * plane;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                store_zero_chunk<QT, W>(p.q, o + 8 * W * m + W * c);
+                store_zero_chunk<KT, W>(p.k, o + 8 * W * m + W * c);
+            }
+#pragma unroll
+            for (int vc = 0; vc < VC; ++vc)
+                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + 64 * vc + 8 * c),
+                      (u32x4){0u, 0u, 0u, 0u});
+        }
+        return;
+    }
+
+    // 1. every data load of the item, before anything that depends on them
+    const uint16_t *tok = p.qkv + (int64_t)b * p.batch_stride + (int64_t)i * p.row_stride;
+    uint32_t rq[HPW][M][W / 2], rk[HPW][M][W / 2];
+    u32x4 rv[HPW][VC];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+        if (u >= nh) break;
+        const int h = h0 + u;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, rq[u][m]);
+            load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, rk[u][m]);
+        }
+#pragma unroll
+        for (int vc = 0; vc < VC; ++vc)
+            rv[u][vc] = *reinterpret_cast<const u32x4 *>(tok + (int64_t)(2 * p.H + h) * D + 64 * vc + 8 * c);
+    }
+    // 2. weights and rotary entries while the loads are in flight
+    float wq[M][W], wk[M][W];
+    load_weights<W, M>(p.wq, c, wq);
+    load_weights<W, M>(p.wk, c, wk);
+    float cs[M][W / 2], sn[M][W / 2];
+    bool rot[M][W / 2];
+    rotary_entries<W, M>(p, b, i, c, cs, sn, rot);
+    const float inv_d = 1.0f / (float)D;
+
+    // 3. normalise, rotate, store
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+        if (u >= nh) break;
+        const int64_t o = orow + u * plane;
+        float xq[M][W], xk[M][W];
+        unpack_row<W, M, IN>(rq[u], xq);
+        unpack_row<W, M, IN>(rk[u], xk);
+        norm_rope_row<W, M>(xq, wq, p.eps, inv_d, cs, sn, rot);
+        norm_rope_row<W, M>(xk, wk, p.eps, inv_d, cs, sn, rot);
+        if constexpr (MODE == MODE_CAST) {
+            float qq[2][M][W];
+            bool slow[2][M][W];
+            bool any = !fast;
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int q = 0; q < W / 2; ++q) {
-                    const int a = paxis[m][q];
-                    const int idx = (a == 0 ? rowoff[0] : (a == 1 ? rowoff[1] : rowoff[2])) + pj[m][q];
-                    cs[m][q] = rot[m][q] ? p.cos_tab[idx] : 1.0f;
-                    sn[m][q] = rot[m][q] ? p.sin_tab[idx] : 0.0f;
+                for (int k = 0; k < W; ++k) {
+                    qq[0][m][k] = quotient_fast(xq[m][k], rcp[0], &slow[0][m][k]);
+                    qq[1][m][k] = quotient_fast(xk[m][k], rcp[1], &slow[1][m][k]);
+                    any = any || slow[0][m][k] || slow[1][m][k];
                 }
-        }
-
-        const uint16_t *tok = p.qkv + (int64_t)b * p.batch_stride + (int64_t)i * p.row_stride;
-        if (!valid) {
-            if constexpr (MODE != MODE_AMAX) {
-                for (int h = h0; h < h1; ++h) {
-                    const int64_t orow = (((int64_t)b * p.H + h) * p.T + i) * D;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        store_zero_chunk<QT, W>(p.q, orow + 8 * W * m + W * c);
-                        store_zero_chunk<KT, W>(p.k, orow + 8 * W * m + W * c);
-                    }
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-                        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.v) + orow + 64 * vc + 8 * c) =
-                            make_uint4(0, 0, 0, 0);
-                }
-            }
-            continue;
-        }
-        // heads in batches of U: every load of the batch is issued before its first use
-        for (int hb = h0; hb < h1; hb += U) {
-            uint32_t rq[U][M][W / 2], rk[U][M][W / 2];
-            uint4 rv[U][VC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int h = hb + u;
-                if (h >= h1) break;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, rq[u][m]);
-                    load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, rk[u][m]);
-                }
-                if constexpr (MODE != MODE_AMAX) {
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-                        rv[u][vc] = *reinterpret_cast<const uint4 *>(tok + (int64_t)(2 * p.H + h) * D + 64 * vc + 8 * c);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int h = hb + u;
-                if (h >= h1) break;
-                float xq[M][W], xk[M][W];
+            if (any) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int k = 0; k < W / 2; ++k) {
-                        xq[m][2 * k] = in_to_f32<IN>(rq[u][m][k] & 0xFFFFu);
-                        xq[m][2 * k + 1] = in_to_f32<IN>(rq[u][m][k] >> 16);
-                        xk[m][2 * k] = in_to_f32<IN>(rk[u][m][k] & 0xFFFFu);
-                        xk[m][2 * k + 1] = in_to_f32<IN>(rk[u][m][k] >> 16);
+                    for (int k = 0; k < W; ++k) {
+                        if (!fast || slow[0][m][k]) qq[0][m][k] = xq[m][k] / ds[0];
+                        if (!fast || slow[1][m][k]) qq[1][m][k] = xk[m][k] / ds[1];
                     }
-                norm_rope_row<W, M>(xq, wq, p.eps, inv_d, cs, sn, rot);
-                norm_rope_row<W, M>(xk, wk, p.eps, inv_d, cs, sn, rot);
-                if constexpr (MODE == MODE_AMAX) {
+            }
+            if constexpr (kPairStore<DT_E4M3, W, M>) {
+                store_row_pairs<DT_E4M3, W>(p.q, o, c, qq[0]);
+                store_row_pairs<DT_E4M3, W>(p.k, o, c, qq[1]);
+            } else {
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
-#pragma unroll
-                        for (int k = 0; k < W; ++k) {
-                            mx[0] = max(mx[0], __float_as_uint(xq[m][k]) & 0x7FFFFFFFu);
-                            mx[1] = max(mx[1], __float_as_uint(xk[m][k]) & 0x7FFFFFFFu);
-                        }
-                } else {
-                    if constexpr (MODE == MODE_CAST) {
-#pragma unroll
-                        for (int m = 0; m < M; ++m)
-#pragma unroll
-                            for (int k = 0; k < W; ++k) {
-                                xq[m][k] = xq[m][k] / ds[0];
-                                xk[m][k] = xk[m][k] / ds[1];
-                            }
-                    }
-                    const int64_t orow = (((int64_t)b * p.H + h) * p.T + i) * D;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        store_chunk<QT, W>(p.q, orow + 8 * W * m + W * c, xq[m]);
-                        store_chunk<KT, W>(p.k, orow + 8 * W * m + W * c, xk[m]);
-                    }
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-                        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.v) + orow + 64 * vc + 8 * c) = rv[u][vc];
+                for (int m = 0; m < M; ++m) {
+                    store_chunk<DT_E4M3, W>(p.q, o + 8 * W * m + W * c, qq[0][m]);
+                    store_chunk<DT_E4M3, W>(p.k, o + 8 * W * m + W * c, qq[1][m]);
                 }
             }
+        } else {
+            if constexpr (kPairStore<QT, W, M>) {
+                store_row_pairs<QT, W>(p.q, o, c, xq);
+            } else {
+#pragma unroll
+                for (int m = 0; m < M; ++m) store_chunk<QT, W>(p.q, o + 8 * W * m + W * c, xq[m]);
+            }
+            if constexpr (kPairStore<KT, W, M>) {
+                store_row_pairs<KT, W>(p.k, o, c, xk);
+            } else {
+#pragma unroll
+                for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + 8 * W * m + W * c, xk[m]);
+            }
+        }
+#pragma unroll
+        for (int vc = 0; vc < VC; ++vc)
+            st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + 64 * vc + 8 * c), rv[u][vc]);
+    }
+}
+
+// ------------------------------------------------------------------ amax kernel
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+template <int D, int W, int M, int HPW>
+struct AmaxItem {
+    uint32_t rq[HPW][M][W / 2], rk[HPW][M][W / 2];
+    int b, i, h0, nh;
+    bool live;  // a valid token of an existing item
+};
+
+template <int D, int W, int M, int HPW>
+__device__ __forceinline__ void amax_fetch(const QkParams &p, int64_t item, int g, int c,
+                                           AmaxItem<D, W, M, HPW> &it) {
+    it.live = false;
+    if (item >= p.items) return;
+    const uint32_t it32 = (uint32_t)item;  // items < 2^31 (checked on the host)
+    const uint32_t bgi = it32 / (uint32_t)p.head_chunks;
+    const int hc = (int)(it32 - bgi * (uint32_t)p.head_chunks);
+    const uint32_t b32 = bgi / (uint32_t)p.groups;
+    it.b = (int)b32;
+    it.i = (int)(bgi - b32 * (uint32_t)p.groups) * 8 + g;
+    it.h0 = hc * HPW;
+    it.nh = min(HPW, p.H - it.h0);
+    if (it.i >= p.T || it.i >= p.vlen[it.b]) return;
+    it.live = true;
+    const uint16_t *tok = p.qkv + (int64_t)it.b * p.batch_stride + (int64_t)it.i * p.row_stride;
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+        if (u >= it.nh) break;
+        const int h = it.h0 + u;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, it.rq[u][m]);
+            load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, it.rk[u][m]);
         }
     }
-    if constexpr (MODE == MODE_AMAX) {
-        const uint32_t m0 = wave_max_u32(mx[0]);
-        const uint32_t m1 = wave_max_u32(mx[1]);
-        if (lane == 0) {
-            if (m0) atomicMax(reinterpret_cast<unsigned int *>(p.amax), m0);
-            if (m1) atomicMax(reinterpret_cast<unsigned int *>(p.amax) + 1, m1);
+}
+
+template <int D, int IN>
+__global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
+    // nothing is stored, so 4-wide chunks: fewer cross-lane tree levels per element than W = 8
+    constexpr int W = 4;
+    constexpr int M = D / (8 * W);
+    constexpr int HPW = kHeadsPerWave;
+    const int lane = threadIdx.x & 63;
+    const int c = chunk_of_lane(lane & 7);  // chunk of the row this lane holds
+    const int g = lane >> 3;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
+    const float inv_d = 1.0f / (float)D;
+
+    float wq[M][W], wk[M][W];
+    load_weights<W, M>(p.wq, c, wq);
+    load_weights<W, M>(p.wk, c, wk);
+    uint32_t mx0 = 0u, mx1 = 0u;  // max of |y'| bits: NaN above +inf above every finite value
+
+    AmaxItem<D, W, M, HPW> cur, nxt;
+    amax_fetch(p, wave0, g, c, cur);
+    for (int64_t item = wave0; item < p.items; item += nwaves) {
+        amax_fetch(p, item + nwaves, g, c, nxt);  // next item's loads in flight
+        if (cur.live) {
+            float cs[M][W / 2], sn[M][W / 2];
+            bool rot[M][W / 2];
+            rotary_entries<W, M>(p, cur.b, cur.i, c, cs, sn, rot);
+#pragma unroll
+            for (int u = 0; u < HPW; ++u) {
+                if (u >= cur.nh) break;
+                float xq[M][W], xk[M][W];
+                unpack_row<W, M, IN>(cur.rq[u], xq);
+                unpack_row<W, M, IN>(cur.rk[u], xk);
+                norm_rope_row<W, M>(xq, wq, p.eps, inv_d, cs, sn, rot);
+                norm_rope_row<W, M>(xk, wk, p.eps, inv_d, cs, sn, rot);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int k = 0; k < W; ++k) {
+                        mx0 = max(mx0, __float_as_uint(xq[m][k]) & 0x7FFFFFFFu);
+                        mx1 = max(mx1, __float_as_uint(xk[m][k]) & 0x7FFFFFFFu);
+                    }
+            }
         }
+        cur = nxt;
+    }
+    __shared__ uint32_t red[2][4];
+    mx0 = wave_max_u32(mx0);
+    mx1 = wave_max_u32(mx1);
+    if (lane == 0) {
+        red[0][wv] = mx0;
+        red[1][wv] = mx1;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+        const int nw = blockDim.x >> 6;
+        uint32_t m = 0u;
+        for (int w = 0; w < nw; ++w) m = max(m, red[threadIdx.x][w]);
+        if (m) atomicMax(reinterpret_cast<unsigned int *>(p.amax) + threadIdx.x, m);
     }
 }
 
@@ -387,42 +614,80 @@ __global__ void clear2_kernel(float *a) {
 
 // ------------------------------------------------------------------ dispatch
 
-template <int D, int IN, int QT, int KT, int MODE>
-int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
-    auto kern = qk_kernel<D, IN, QT, KT, MODE>;
-    static int max_blocks = 0;  // resident blocks per CU for this instantiation
-    static int cus = 0;
-    if (max_blocks == 0) {
+// Device facts read once per process (all devices of one process are gfx950 parts).
+struct DeviceFacts {
+    int cus = 0;
+    int lds_per_cu = 0;
+};
+
+bool device_facts(DeviceFacts *f, std::string *err) {
+    static DeviceFacts facts;
+    if (facts.cus == 0) {
         int dev = 0;
+        DeviceFacts t;
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&max_blocks, kern, 256, 0) != hipSuccess ||
-            max_blocks <= 0) {
-            max_blocks = 0;
+            hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&t.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            t.cus <= 0 || t.lds_per_cu <= 0) {
             *err = "device query failed (no HIP device?)";
-            return H3_ELAUNCH;
+            return false;
         }
+        facts = t;
     }
-    const int64_t waves_needed = p.items;
-    int64_t blocks = (waves_needed + 3) / 4;
-    const int64_t cap = (int64_t)max_blocks * cus;
-    if (blocks > cap) blocks = cap;
-    if (MODE == MODE_AMAX) {
-        hipLaunchKernelGGL(clear2_kernel, dim3(1), dim3(64), 0, stream, p.amax);
-        hipError_t e0 = hipGetLastError();
-        if (e0 != hipSuccess) {
-            *err = std::string("amax clear launch failed: ") + hipGetErrorString(e0);
-            return H3_ELAUNCH;
-        }
+    *f = facts;
+    return true;
+}
+
+int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err) {
+    if (blocks <= 0) return H3_OK;
+    if (blocks > 0x7FFFFFFF) {
+        *err = "problem too large for one launch";
+        return H3_EUNSUPPORTED;
     }
     void *args[] = {&p};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3((unsigned)blocks),
-                                   dim3(256), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, lds, stream);
     if (e != hipSuccess) {
         *err = std::string("kernel launch failed: ") + hipGetErrorString(e);
         return H3_ELAUNCH;
     }
     return H3_OK;
+}
+
+// Resident blocks per CU of the store / cast kernels.  They stream with no reuse, and on MI355X
+// fewer concurrent blocks keep a narrower window of every output plane open in HBM: 3 blocks
+// (12 waves) per CU measured best for the full-latent workload (4-5 within 1 %, 6-7 about 7 %
+// slower).  The cap is imposed by reserving a third of the CU's LDS per block (the kernels use none).
+constexpr int kStoreBlocksPerCU = 3;
+
+template <int D, int IN, int QT, int KT, int MODE>
+int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
+    DeviceFacts f;
+    if (!device_facts(&f, err)) return H3_ELAUNCH;
+    if constexpr (MODE == MODE_AMAX) {
+        auto kern = qk_amax_kernel<D, IN>;
+        static int max_blocks = 0;  // resident blocks per CU of this kernel
+        if (max_blocks == 0 &&
+            (hipOccupancyMaxActiveBlocksPerMultiprocessor(&max_blocks, kern, 256, 0) != hipSuccess || max_blocks <= 0)) {
+            max_blocks = 0;
+            *err = "occupancy query failed";
+            return H3_ELAUNCH;
+        }
+        hipLaunchKernelGGL(clear2_kernel, dim3(1), dim3(64), 0, stream, p.amax);
+        const hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) {
+            *err = std::string("amax clear launch failed: ") + hipGetErrorString(e0);
+            return H3_ELAUNCH;
+        }
+        // persistent waves, two rounds of resident blocks: one atomic per block and tensor
+        int64_t blocks = (p.items + 3) / 4;
+        const int64_t cap = 2 * (int64_t)max_blocks * f.cus;
+        if (blocks > cap) blocks = cap;
+        return launch_kernel(reinterpret_cast<const void *>(kern), blocks, 0, p, stream, err);
+    } else {
+        auto kern = qk_kernel<D, IN, QT, KT, MODE>;
+        const size_t lds = (size_t)(f.lds_per_cu / kStoreBlocksPerCU);
+        return launch_kernel(reinterpret_cast<const void *>(kern), (p.items + 3) / 4, lds, p, stream, err);
+    }
 }
 
 template <int D, int IN, int MODE>
