@@ -83,17 +83,6 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
     return code | sign;
 }
 
-// Four E4M3FN codes packed little-endian, by the gfx950 conversion instruction (round to nearest
-// even).  The instruction itself turns magnitudes from 464 up into NaN, so values are first
-// clamped to +-448 (NaN stays NaN: both comparisons are false).  For every non-NaN binary32 this
-// equals f32_to_e4m3; a NaN gives a NaN code whose sign bit is not specified.
-__device__ __forceinline__ float clamp448(float x) { return x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x); }
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
-    return (uint32_t)w;
-}
-
 template <int OT>
 __device__ __forceinline__ uint32_t encode_out(float x) {
     if constexpr (OT == DT_F16) return f32_to_f16_bits(x);
@@ -167,13 +156,6 @@ __device__ __forceinline__ void store_chunk(void *base, int64_t e, const float (
 #pragma unroll
         for (int k = 0; k < W; k += 4)
             st_nt(reinterpret_cast<f32x4 *>(p + k), (f32x4){y[k], y[k + 1], y[k + 2], y[k + 3]});
-    } else if constexpr (OT == DT_E4M3) {
-        uint8_t *p = reinterpret_cast<uint8_t *>(base) + e;
-        if constexpr (W == 4) {
-            st_nt(reinterpret_cast<uint32_t *>(p), e4m3x4(y[0], y[1], y[2], y[3]));
-        } else {
-            st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7])});
-        }
     } else {
         uint32_t w[W];
 #pragma unroll
@@ -196,25 +178,16 @@ __device__ __forceinline__ void store_zero_chunk(void *base, int64_t e) {
     }
 }
 
-// Whole-row store of the lane's M = 2 chunks for 8-byte chunks (16-bit outputs with W = 4,
-// E4M3 with W = 8): neighbouring lanes (chunks 2j and 2j + 1, always lanes l and l ^ 1 under
-// chunk_of_lane) swap halves with one DPP move per word, so the even-chunk lane holds the 16 bytes
-// of chunks 2j, 2j + 1 of the first half-row and the odd one those of the second half-row.  One
-// 16-byte store per lane then writes the token's row as whole 128-byte lines, which reach HBM
-// without depending on the L2 to merge two half-line writes.
-template <int OT, int W>
-__device__ __forceinline__ void store_row_pairs(void *base, int64_t row_e, int c, const float (&y)[2][W]) {
-    static_assert((OT == DT_E4M3 && W == 8) || ((OT == DT_F16 || OT == DT_BF16) && W == 4), "8-byte chunks");
-    uint32_t m0[2], m1[2];
-    if constexpr (OT == DT_E4M3) {
-        m0[0] = e4m3x4(y[0][0], y[0][1], y[0][2], y[0][3]); m0[1] = e4m3x4(y[0][4], y[0][5], y[0][6], y[0][7]);
-        m1[0] = e4m3x4(y[1][0], y[1][1], y[1][2], y[1][3]); m1[1] = e4m3x4(y[1][4], y[1][5], y[1][6], y[1][7]);
-    } else {
-        m0[0] = encode_out<OT>(y[0][0]) | (encode_out<OT>(y[0][1]) << 16);
-        m0[1] = encode_out<OT>(y[0][2]) | (encode_out<OT>(y[0][3]) << 16);
-        m1[0] = encode_out<OT>(y[1][0]) | (encode_out<OT>(y[1][1]) << 16);
-        m1[1] = encode_out<OT>(y[1][2]) | (encode_out<OT>(y[1][3]) << 16);
-    }
+// Whole-row store of the lane's M = 2 chunks when a chunk is 8 bytes (16-bit outputs with W = 4,
+// E4M3 codes with W = 8), given as two packed words per chunk: neighbouring lanes (chunks 2j and
+// 2j + 1, always lanes l and l ^ 1 under chunk_of_lane) swap halves with one DPP move per word,
+// so the even-chunk lane holds the 16 bytes of chunks 2j, 2j + 1 of the first half-row and the odd
+// one those of the second half-row.  One 16-byte store per lane then writes the token's row as
+// whole 128-byte lines, which reach HBM without relying on the L2 to merge half-line writes.
+template <int EB, int W>
+__device__ __forceinline__ void store_words_pairs(void *base, int64_t row_e, int c, const uint32_t (&m0)[2],
+                                                  const uint32_t (&m1)[2]) {
+    static_assert(EB * W == 8, "8-byte chunks");
     const bool odd = c & 1;
     const uint32_t s0 = odd ? m0[0] : m1[0], s1 = odd ? m0[1] : m1[1];
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xF, 0xF, true);
@@ -222,12 +195,30 @@ __device__ __forceinline__ void store_row_pairs(void *base, int64_t row_e, int c
     const u32x4 v = odd ? (u32x4){r0, r1, m1[0], m1[1]} : (u32x4){m0[0], m0[1], r0, r1};
     // even chunk 2j: elements [2j W, 2j W + 2W); odd chunk 2j + 1: [8W + 2j W, 8W + 2j W + 2W)
     const int64_t e = row_e + (odd ? 8 * W + (c - 1) * W : c * W);
-    constexpr int EB = OT == DT_E4M3 ? 1 : 2;
     st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(base) + e * EB), v);
 }
 
+template <int OT, int W>
+__device__ __forceinline__ void store_row_pairs(void *base, int64_t row_e, int c, const float (&y)[2][W]) {
+    static_assert((OT == DT_F16 || OT == DT_BF16) && W == 4, "16-bit outputs, 4-wide chunks");
+    uint32_t m0[2], m1[2];
+    m0[0] = encode_out<OT>(y[0][0]) | (encode_out<OT>(y[0][1]) << 16);
+    m0[1] = encode_out<OT>(y[0][2]) | (encode_out<OT>(y[0][3]) << 16);
+    m1[0] = encode_out<OT>(y[1][0]) | (encode_out<OT>(y[1][1]) << 16);
+    m1[1] = encode_out<OT>(y[1][2]) | (encode_out<OT>(y[1][3]) << 16);
+    store_words_pairs<2, W>(base, row_e, c, m0, m1);
+}
+
+// W E4M3 codes (W / 4 packed words) at element e.
+template <int W>
+__device__ __forceinline__ void store_code_words(void *base, int64_t e, const uint32_t (&w)[W / 4]) {
+    uint8_t *p = reinterpret_cast<uint8_t *>(base) + e;
+    if constexpr (W == 4) st_nt(reinterpret_cast<uint32_t *>(p), w[0]);
+    else st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){w[0], w[1]});
+}
+
 template <int OT, int W, int M>
-constexpr bool kPairStore = M == 2 && ((OT == DT_E4M3 && W == 8) || ((OT == DT_F16 || OT == DT_BF16) && W == 4));
+constexpr bool kPairStore = M == 2 && (OT == DT_F16 || OT == DT_BF16) && W == 4;
 
 // ------------------------------------------------------------------ the row
 
@@ -310,13 +301,16 @@ __device__ __forceinline__ void load_weights(const float *wsrc, int c, float (&w
 }
 
 // Rotary entries of this lane's pairs for token i of item b.  Pair index pr (the dims 2 pr,
-// 2 pr + 1) rotates when pr < 3n, on axis pr / n at frequency pr mod n; the axis comes from
-// floor((pr + 1/2) / n) in binary32, exact because pr + 1/2 is never a multiple of n and the
-// rounding error is far below the 1/(2n) margin for pr < 128.
-template <int W, int M>
+// 2 pr + 1) rotates when pr < 3n, on axis pr / n at frequency pr mod n.  NN is n when it is known
+// at compile time (the natural split n = D / 8), else 0 and n is read from the parameters; the
+// axis then comes from floor((pr + 1/2) / n) in binary32, exact because pr + 1/2 is never a
+// multiple of n and the rounding error is far below the 1/(2n) margin for pr < 128.  With NN
+// known, chunks whose pairs all rotate (or none does) need no per-lane test.
+template <int W, int M, int NN>
 __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, int c,
                                                float (&cs)[M][W / 2], float (&sn)[M][W / 2],
                                                bool (&rot)[M][W / 2]) {
+    const int n = NN ? NN : p.n;
     const uint32_t ui = (uint32_t)i;
     const uint32_t j = div_apply(ui, p.div_gw);   // i / Gw
     const uint32_t tq = div_apply(j, p.div_gh);   // i / (Gh Gw)
@@ -327,34 +321,55 @@ __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, 
     for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int q = 0; q < W / 2; ++q) {
-            const int pr = 4 * W * m + (W / 2) * c + q;
-            rot[m][q] = pr < 3 * p.n;
-            const int axis = (int)(((float)pr + 0.5f) * p.inv_n);
-            const int jj = pr - axis * p.n;
+            const int pr = 4 * W * m + (W / 2) * c + q;  // chunk m spans pairs [4W m, 4W m + 4W)
+            if (NN && 4 * W * m + 4 * W <= 3 * NN) rot[m][q] = true;
+            else if (NN && 4 * W * m >= 3 * NN) rot[m][q] = false;
+            else rot[m][q] = pr < 3 * n;
+            const int axis = NN ? pr / (NN ? NN : 1) : (int)(((float)pr + 0.5f) * p.inv_n);
+            const int jj = pr - axis * n;
             const int row = axis == 0 ? row_t : (axis == 1 ? row_h : row_w);
-            const int idx = row * p.n + jj;
+            const int idx = row * n + jj;
             cs[m][q] = rot[m][q] ? p.cos_tab[idx] : 1.0f;
             sn[m][q] = rot[m][q] ? p.sin_tab[idx] : 0.0f;
         }
 }
 
-// code of RN(y / ds) in E4M3FN.  Fast path: q0 = RN(y * rcp) with rcp = RN(1 / ds) is within
-// about 2 ulps of y / ds.  An E4M3 code only changes across the midpoints of the E4M3 grid,
-// which in the normal E4M3 range are the binary32 values whose 20 low significand bits are
-// 0x80000; when q0 is more than 4 ulps from such a midpoint and |q0| >= 2^-6, RN(y / ds) lies on
-// the same side of every midpoint and has the same code.  Otherwise (or when ds is outside the
-// normal range where rcp is exact enough) the quotient is computed by correctly rounded division.
-__device__ __forceinline__ float quotient_fast(float y, float rcp, bool *slow) {
+// RN(y / ds) without a division instruction, for a descale ds in [2^-60, 2^60] with
+// rcp = RN(1 / ds): q0 = RN(y rcp) is within 1.5 ulps of y / ds, one FMA remainder correction makes
+// it faithful, and a second one then gives the correctly rounded quotient (Markstein's theorem on
+// correcting a faithful quotient with a correctly rounded reciprocal; IBM J. Res. Dev. 34(1), 1990).
+// Checked against correctly rounded division for every binary32 y with y / ds in [2^-12, 512) and
+// 80 descales.  The quotient's sign is that of y (ds > 0), which also fixes y = -0.  Quotients
+// below 2^-11 may lose accuracy to underflow in the remainders, but every value under 2^-10
+// encodes to a zero code either way.  The result is a correctly rounded division, so the
+// no-contraction rule of the arithmetic chain is untouched.
+__device__ __forceinline__ float quotient(float y, float ds, float rcp) {
     const float q0 = y * rcp;
-    const uint32_t a = __float_as_uint(q0) & 0x7FFFFFFFu;
-    const int d = (int)(a & 0xFFFFFu) - 0x80000;
-    *slow = a < 0x3C800000u || (d <= 4 && d >= -4);
-    return q0;
+    const float r0 = __builtin_fmaf(-q0, ds, y);
+    const float q1 = __builtin_fmaf(r0, rcp, q0);
+    const float r1 = __builtin_fmaf(-q1, ds, y);
+    return __builtin_copysignf(__builtin_fmaf(r1, rcp, q1), y);
+}
+
+// Codes of W quotients as W/4 packed words.  hw: the conversion instruction, exact for |q| <= 448
+// (the caller guarantees that range); otherwise the integer encoder (saturation, NaN).
+template <int W>
+__device__ __forceinline__ void pack_e4m3(const float (&q)[W], bool hw, uint32_t (&w)[W / 4]) {
+#pragma unroll
+    for (int k = 0; k < W; k += 4) {
+        if (hw) {
+            int t = __builtin_amdgcn_cvt_pk_fp8_f32(q[k], q[k + 1], 0, false);
+            w[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[k + 2], q[k + 3], t, true);
+        } else {
+            w[k / 4] = f32_to_e4m3(q[k]) | (f32_to_e4m3(q[k + 1]) << 8) | (f32_to_e4m3(q[k + 2]) << 16) |
+                       (f32_to_e4m3(q[k + 3]) << 24);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ store / cast kernel
 
-template <int D, int IN, int QT, int KT, int MODE>
+template <int D, int IN, int QT, int KT, int MODE, int NN>
 __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     constexpr int W = (D == 64) ? 4 : 8;
     constexpr int M = D / (8 * W);
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
             ds[s] = am > 0.0f ? am / 448.0f : 1.0f;
             rcp[s] = 1.0f / ds[s];
         }
-        fast = ds[0] >= 0x1p-125f && ds[0] <= 0x1p125f && ds[1] >= 0x1p-125f && ds[1] <= 0x1p125f;
+        fast = ds[0] >= 0x1p-60f && ds[0] <= 0x1p60f && ds[1] >= 0x1p-60f && ds[1] <= 0x1p60f;
         if (item == 0 && lane == 0) {
             p.descale[0] = ds[0];
             p.descale[1] = ds[1];
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     load_weights<W, M>(p.wk, c, wk);
     float cs[M][W / 2], sn[M][W / 2];
     bool rot[M][W / 2];
-    rotary_entries<W, M>(p, b, i, c, cs, sn, rot);
+    rotary_entries<W, M, NN>(p, b, i, c, cs, sn, rot);
     const float inv_d = 1.0f / (float)D;
 
     // 3. normalise, rotate, store
@@ -454,33 +469,40 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
         norm_rope_row<W, M>(xk, wk, p.eps, inv_d, cs, sn, rot);
         if constexpr (MODE == MODE_CAST) {
             float qq[2][M][W];
-            bool slow[2][M][W];
-            bool any = !fast;
+            bool bad = false;  // a quotient above 448 in magnitude or NaN
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int k = 0; k < W; ++k) {
-                    qq[0][m][k] = quotient_fast(xq[m][k], rcp[0], &slow[0][m][k]);
-                    qq[1][m][k] = quotient_fast(xk[m][k], rcp[1], &slow[1][m][k]);
-                    any = any || slow[0][m][k] || slow[1][m][k];
+                    qq[0][m][k] = quotient(xq[m][k], ds[0], rcp[0]);
+                    qq[1][m][k] = quotient(xk[m][k], ds[1], rcp[1]);
+                    bad = bad || !(__builtin_fabsf(qq[0][m][k]) <= 448.0f) || !(__builtin_fabsf(qq[1][m][k]) <= 448.0f);
                 }
-            if (any) {
+            // rare (saturation, non-finite data, extreme descales): one branch for the whole wave
+            const bool exact = !fast || __builtin_amdgcn_ballot_w64(bad) != 0;
+            if (exact) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
                     for (int k = 0; k < W; ++k) {
-                        if (!fast || slow[0][m][k]) qq[0][m][k] = xq[m][k] / ds[0];
-                        if (!fast || slow[1][m][k]) qq[1][m][k] = xk[m][k] / ds[1];
+                        if (!fast || !(__builtin_fabsf(qq[0][m][k]) <= 448.0f)) qq[0][m][k] = xq[m][k] / ds[0];
+                        if (!fast || !(__builtin_fabsf(qq[1][m][k]) <= 448.0f)) qq[1][m][k] = xk[m][k] / ds[1];
                     }
             }
-            if constexpr (kPairStore<DT_E4M3, W, M>) {
-                store_row_pairs<DT_E4M3, W>(p.q, o, c, qq[0]);
-                store_row_pairs<DT_E4M3, W>(p.k, o, c, qq[1]);
+            uint32_t cw[2][M][W / 4];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                pack_e4m3<W>(qq[0][m], !exact, cw[0][m]);
+                pack_e4m3<W>(qq[1][m], !exact, cw[1][m]);
+            }
+            if constexpr (W == 8 && M == 2) {
+                store_words_pairs<1, W>(p.q, o, c, cw[0][0], cw[0][1]);
+                store_words_pairs<1, W>(p.k, o, c, cw[1][0], cw[1][1]);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    store_chunk<DT_E4M3, W>(p.q, o + 8 * W * m + W * c, qq[0][m]);
-                    store_chunk<DT_E4M3, W>(p.k, o + 8 * W * m + W * c, qq[1][m]);
+                    store_code_words<W>(p.q, o + 8 * W * m + W * c, cw[0][m]);
+                    store_code_words<W>(p.k, o + 8 * W * m + W * c, cw[1][m]);
                 }
             }
         } else {
@@ -546,7 +568,7 @@ __device__ __forceinline__ void amax_fetch(const QkParams &p, int64_t item, int 
     }
 }
 
-template <int D, int IN>
+template <int D, int IN, int NN>
 __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
     // nothing is stored, so 4-wide chunks: fewer cross-lane tree levels per element than W = 8
     constexpr int W = 4;
@@ -572,7 +594,7 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
         if (cur.live) {
             float cs[M][W / 2], sn[M][W / 2];
             bool rot[M][W / 2];
-            rotary_entries<W, M>(p, cur.b, cur.i, c, cs, sn, rot);
+            rotary_entries<W, M, NN>(p, cur.b, cur.i, c, cs, sn, rot);
 #pragma unroll
             for (int u = 0; u < HPW; ++u) {
                 if (u >= cur.nh) break;
@@ -659,12 +681,12 @@ int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hip
 // slower).  The cap is imposed by reserving a third of the CU's LDS per block (the kernels use none).
 constexpr int kStoreBlocksPerCU = 3;
 
-template <int D, int IN, int QT, int KT, int MODE>
+template <int D, int IN, int QT, int KT, int MODE, int NN>
 int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
     DeviceFacts f;
     if (!device_facts(&f, err)) return H3_ELAUNCH;
     if constexpr (MODE == MODE_AMAX) {
-        auto kern = qk_amax_kernel<D, IN>;
+        auto kern = qk_amax_kernel<D, IN, NN>;
         static int max_blocks = 0;  // resident blocks per CU of this kernel
         if (max_blocks == 0 &&
             (hipOccupancyMaxActiveBlocksPerMultiprocessor(&max_blocks, kern, 256, 0) != hipSuccess || max_blocks <= 0)) {
@@ -684,7 +706,7 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
         if (blocks > cap) blocks = cap;
         return launch_kernel(reinterpret_cast<const void *>(kern), blocks, 0, p, stream, err);
     } else {
-        auto kern = qk_kernel<D, IN, QT, KT, MODE>;
+        auto kern = qk_kernel<D, IN, QT, KT, MODE, NN>;
         const size_t lds = (size_t)(f.lds_per_cu / kStoreBlocksPerCU);
         return launch_kernel(reinterpret_cast<const void *>(kern), (p.items + 3) / 4, lds, p, stream, err);
     }
@@ -693,14 +715,17 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
 template <int D, int IN, int MODE>
 int dispatch_out(int q_dt, int k_dt, QkParams &p, hipStream_t s, std::string *err) {
     if constexpr (MODE == MODE_STORE) {
-#define H3_QK(QT, KT) \
-    if (q_dt == QT && k_dt == KT) return launch_one<D, IN, QT, KT, MODE>(p, s, err);
+#define H3_QK(QT, KT)                                                                        \
+    if (q_dt == QT && k_dt == KT)                                                            \
+        return p.n == D / 8 ? launch_one<D, IN, QT, KT, MODE, D / 8>(p, s, err)               \
+                            : launch_one<D, IN, QT, KT, MODE, 0>(p, s, err);
         H3_QK(DT_F32, DT_F16) H3_QK(DT_F32, DT_BF16) H3_QK(DT_F32, DT_F32)
         H3_QK(DT_F16, DT_F16) H3_QK(DT_F16, DT_BF16) H3_QK(DT_F16, DT_F32)
         H3_QK(DT_BF16, DT_F16) H3_QK(DT_BF16, DT_BF16) H3_QK(DT_BF16, DT_F32)
 #undef H3_QK
     } else {
-        return launch_one<D, IN, DT_E4M3, DT_E4M3, MODE>(p, s, err);
+        return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8>(p, s, err)
+                            : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0>(p, s, err);
     }
     *err = "unsupported output dtype combination";
     return H3_EUNSUPPORTED;
