@@ -123,8 +123,9 @@ int h3_qk_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
 /*
  * FP8 cast pass ([TRT-21485] Summary and fused_fp8_qk commit):
  *   descale_s = amax_qk[s] / 448 if amax_qk[s] > 0, else 1   (read on the device, no host sync)
- *   q_codes / k_codes  DEVICE uint8 [B, H, T, D]: E4M3FN(y' / descale_s), round to nearest
- *                      even, saturating to +-448; 0x00 for padding tokens
+ *   q_codes / k_codes  DEVICE uint8 [B, H, T, D]: E4M3FN(RN(y' / descale_s)), round to nearest
+ *                      even, saturating to +-448 (also +-inf); a NaN gives a NaN code (0x7F or
+ *                      0xFF, sign not specified); 0x00 for padding tokens
  *   v_out              DEVICE [B, H, T, D], dtype in_dt: bit copy of the V heads (+0 for padding)
  *   descale_qk         DEVICE fp32 [2] out: the two descales for the attention consumer
  *   amax_qk            DEVICE fp32 [2] in (from h3_qk_amax, or 448 * a static descale)
