@@ -135,6 +135,48 @@ def bench_fp8(wl, steps, warmup):
             "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1)}
 
 
+def bench_block_ops(steps, warmup, rotate=8):
+    """SwiGLU on [1797, 2 x 8192] f16 and the scaled residual on [2 x 1797, 2048] (fp32 residual,
+    f16 branch, per-channel scale), each with `rotate` buffer sets so the 256 MB MALL holds none."""
+    import numpy as np
+    import torch
+
+    import rmsnorm_rope_amd as h3
+    import synth
+    stream = torch.cuda.current_stream()
+    N, F = synth.SWIGLU_SHAPE
+    xb = synth.swiglu_input(N, F)
+    xs = [torch.from_numpy(xb.view(np.int16).copy()).cuda() for _ in range(rotate)]
+    ys = [torch.empty((N, F), dtype=torch.int16, device="cuda") for _ in range(rotate)]
+    it = [0]
+
+    def sw():
+        j = it[0] % rotate
+        it[0] += 1
+        h3.h3_swiglu(xs[j], "f16", ys[j], N, F, stream=stream.cuda_stream)
+
+    _, psw = time_launches(sw, steps, warmup, stream)
+    Nr, C = synth.RESIDUAL_SHAPE
+    res, br, sc = synth.residual_inputs(Nr, C)
+    rs = [torch.from_numpy(res).cuda() for _ in range(rotate)]
+    bs = [torch.from_numpy(br.view(np.int16).copy()).cuda() for _ in range(rotate)]
+    os_ = [torch.empty_like(rs[0]) for _ in range(rotate)]
+    s = torch.from_numpy(sc).cuda()
+
+    def rr():
+        j = it[0] % rotate
+        it[0] += 1
+        h3.h3_scaled_residual(rs[j], bs[j], "f16", s, C, os_[j], Nr, C, stream=stream.cuda_stream)
+
+    _, prr = time_launches(rr, steps, warmup, stream)
+    bsw, brr = N * F * 6, Nr * C * 10
+    return {"swiglu": {"shape": [N, 2 * F], "kernel_us": round(psw * 1e3, 2), "GBs": round(bsw / psw / 1e6, 1),
+                       "frac_of_peak": round(bsw / psw / 1e6 / HBM_PEAK_GBS, 4), "buffer_sets_rotated": rotate},
+            "scaled_residual": {"shape": [Nr, C], "kernel_us": round(prr * 1e3, 2), "GBs": round(brr / prr / 1e6, 1),
+                                "frac_of_peak": round(brr / prr / 1e6 / HBM_PEAK_GBS, 4),
+                                "buffer_sets_rotated": rotate}}
+
+
 def pmc_summary(root):
     """Write profiles/traffic_latent.txt from four rocprofv3 --pmc runs under `root`:
     pmc_FETCH_SIZE, pmc_WRITE_SIZE (this bench) and pmccopy_FETCH_SIZE, pmccopy_WRITE_SIZE
@@ -264,6 +306,7 @@ def main():
                            "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
                            "buffer_sets_rotated": rot}
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
+        extra.update(bench_block_ops(max(20, args.steps), args.warmup))
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pb)

@@ -135,6 +135,29 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
                     uint8_t *q_codes, uint8_t *k_codes, void *v_out, float *descale_qk,
                     hipStream_t stream);
 
+/*
+ * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,
+ * SwiGLU row: SiluAndMul after the FP16 w1 output):
+ *   x  DEVICE dt [N][2F] row-major: gate g = x[:, :F], up u = x[:, F:]
+ *   y  DEVICE dt [N][F]:  y = RN_dt( (g / (1 + exp(-g))) * u ), every step in binary32
+ * dt is H3_F16 or H3_BF16; F a multiple of 8; N * F / 8 < 2^32; x, y 16-byte aligned, not
+ * overlapping.  exp is the device library's binary32 exp (about 1 ulp), so y may differ by one
+ * ulp of dt from the exactly rounded value.
+ */
+int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream);
+
+/*
+ * Scaled residual ([OMNI-6607] Operations table: FP32 residual + FP16 branch * FP32 scale, with
+ * contraction disabled):
+ *   out[n][c] = res[n][c] + (branch[n][c] * scale[scale_len == 1 ? 0 : c])
+ * in binary32, the product rounded before the sum.  res, out DEVICE fp32 [N][C]; branch DEVICE
+ * branch_dt (H3_F16 or H3_BF16) [N][C]; scale DEVICE fp32 [scale_len], scale_len 1 or C.  C a
+ * multiple of 4; N * C / 4 < 2^32; res, out, scale 16-byte and branch 8-byte aligned; out overlaps
+ * no input.
+ */
+int h3_scaled_residual(const float *res, const void *branch, h3_dtype branch_dt, const float *scale,
+                       int64_t scale_len, float *out, int64_t N, int64_t C, hipStream_t stream);
+
 /* Thread-local text of the last error of an h3_* call on this thread ("" after success);
    valid until the next h3_* call on the same thread. */
 const char *h3_last_error(void);

@@ -63,6 +63,12 @@ def lib():
         L.h3ref_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.h3ref_e4m3_decode.restype = ctypes.c_float
         L.h3ref_e4m3_encode_array.argtypes = [fp, vp, i64]
+        L.h3ref_f16_encode_f64.argtypes = [ctypes.c_double]
+        L.h3ref_f16_encode_f64.restype = ctypes.c_uint16
+        L.h3ref_bf16_encode_f64.argtypes = [ctypes.c_double]
+        L.h3ref_bf16_encode_f64.restype = ctypes.c_uint16
+        L.h3ref_swiglu.argtypes = [vp, vp, i64, i64, ctypes.c_int]
+        L.h3ref_scaled_residual.argtypes = [fp, vp, fp, i64, fp, i64, i64, ctypes.c_int]
         L.h3ref_descale.argtypes = [ctypes.c_float]
         L.h3ref_descale.restype = ctypes.c_float
         _lib = L
@@ -231,3 +237,30 @@ def decode(bits: np.ndarray, dt: str) -> np.ndarray:
 
 def descale(amax: float) -> float:
     return lib().h3ref_descale(ctypes.c_float(amax))
+
+
+def swiglu(x_bits: np.ndarray, in_dt: str = "f16") -> np.ndarray:
+    """x_bits [N, 2F] 16-bit -> y bits [N, F]: silu(gate) * up in binary64, one rounding."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    N, F2 = x.shape
+    y = np.empty((N, F2 // 2), np.uint16)
+    lib().h3ref_swiglu(_ptr(x), _ptr(y), N, F2 // 2, DT[in_dt])
+    return y
+
+
+def scaled_residual(res: np.ndarray, branch_bits: np.ndarray, scale: np.ndarray, in_dt: str = "f16") -> np.ndarray:
+    res = np.ascontiguousarray(res, dtype=np.float32)
+    br = np.ascontiguousarray(branch_bits, dtype=np.uint16)
+    sc = np.ascontiguousarray(scale, dtype=np.float32).ravel()
+    N, C = res.shape
+    out = np.empty_like(res)
+    lib().h3ref_scaled_residual(_ptr(res), _ptr(br), _ptr(sc), sc.size, _ptr(out), N, C, DT[in_dt])
+    return out
+
+
+def f16_encode_f64(v: float) -> int:
+    return lib().h3ref_f16_encode_f64(ctypes.c_double(v))
+
+
+def bf16_encode_f64(v: float) -> int:
+    return lib().h3ref_bf16_encode_f64(ctypes.c_double(v))

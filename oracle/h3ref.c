@@ -353,3 +353,71 @@ int h3ref_qk_tokens(const h3ref_problem *P, const void *qkv_rows, int in_dt, con
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ decoder-block elementwise ops
+ * vllm-omni PR #6607, "Operations" table, SwiGLU and scaled-residual rows (and the B300 isolated
+ * measurements in the review thread): SwiGLU is SiluAndMul applied to the FP16 output of w1 (gate =
+ * first half of the last dim, up = second half); the scaled residual is an FP32 residual plus the
+ * FP16 branch times an FP32 scale, with contraction disabled.
+ */
+
+/* binary64 -> binary16, one rounding to nearest even (overflow to infinity, NaN stays NaN). */
+uint16_t h3ref_f16_encode_f64(double v) {
+    uint64_t x; memcpy(&x, &v, 8);
+    uint16_t sign = (uint16_t)((x >> 48) & 0x8000);
+    uint64_t a = x & 0x7FFFFFFFFFFFFFFFull;
+    if (a > 0x7FF0000000000000ull) return (uint16_t)(sign | 0x7E00);
+    if (a == 0) return sign;
+    int E = (int)(a >> 52);
+    uint64_t sig = (a & 0xFFFFFFFFFFFFFull) | (E ? (1ull << 52) : 0);
+    int e = E ? E - 1023 : -1022;
+    if (e > 15) return (uint16_t)(sign | 0x7C00);
+    uint64_t code;
+    if (e >= -14) code = ((uint64_t)(e + 14) << 10) + rne_shift(sig, 42);
+    else code = rne_shift(sig, 42 + (-14 - e));
+    if (code >= 0x7C00) code = 0x7C00;  /* rounded past 65504 */
+    return (uint16_t)(sign | code);
+}
+
+/* binary64 -> bfloat16, one rounding to nearest even (overflow to infinity, NaN stays NaN). */
+uint16_t h3ref_bf16_encode_f64(double v) {
+    uint64_t x; memcpy(&x, &v, 8);
+    uint16_t sign = (uint16_t)((x >> 48) & 0x8000);
+    uint64_t a = x & 0x7FFFFFFFFFFFFFFFull;
+    if (a > 0x7FF0000000000000ull) return (uint16_t)(sign | 0x7FC0);
+    if (a == 0) return sign;
+    int E = (int)(a >> 52);
+    uint64_t sig = (a & 0xFFFFFFFFFFFFFull) | (E ? (1ull << 52) : 0);
+    int e = E ? E - 1023 : -1022;
+    if (e > 127) return (uint16_t)(sign | 0x7F80);
+    uint64_t code;
+    if (e >= -126) code = ((uint64_t)(e + 126) << 7) + rne_shift(sig, 45);
+    else code = rne_shift(sig, 45 + (-126 - e));
+    if (code >= 0x7F80) code = 0x7F80;  /* rounded past the largest finite value */
+    return (uint16_t)(sign | code);
+}
+
+/* y = silu(g) * u with g = x[:, :F], u = x[:, F:], silu(g) = g / (1 + exp(-g)), evaluated in binary64
+   (libm exp) and rounded once to binary16.  x, y are binary16 bits; x is [N][2F], y is [N][F]. */
+void h3ref_swiglu(const uint16_t *x, uint16_t *y, int64_t N, int64_t F, int in_dt) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t f = 0; f < F; ++f) {
+            double g = load_in(x, in_dt, n * 2 * F + f);
+            double u = load_in(x, in_dt, n * 2 * F + F + f);
+            double s = g / (1.0 + exp(-g));
+            double v = s * u;
+            y[n * F + f] = in_dt == REF_BF16 ? h3ref_bf16_encode_f64(v) : h3ref_f16_encode_f64(v);
+        }
+}
+
+/* out[n][c] = res[n][c] + (branch[n][c] * scale[c or 0]) in binary32: the product rounded, then the
+   sum (no fused multiply-add).  branch is 16-bit (in_dt), res / scale / out are fp32. */
+void h3ref_scaled_residual(const float *res, const uint16_t *branch, const float *scale, int64_t scale_len,
+                           float *out, int64_t N, int64_t C, int in_dt) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t c = 0; c < C; ++c) {
+            float b = load_in(branch, in_dt, n * C + c);
+            float t = b * scale[scale_len == 1 ? 0 : c];
+            out[n * C + c] = res[n * C + c] + t;
+        }
+}

@@ -13,7 +13,8 @@ from typing import Optional, Sequence
 
 __all__ = [
     "F32", "F16", "BF16", "E4M3FN", "MAX_BATCH", "H3Error", "QkDesc", "make_desc", "lib",
-    "h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_last_error", "h3_abi_version",
+    "h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_swiglu", "h3_scaled_residual",
+    "h3_last_error", "h3_abi_version",
     "EXPORTS",
 ]
 
@@ -26,8 +27,8 @@ ERRORS = {0: "H3_OK", -1: "H3_EINVAL", -2: "H3_EUNSUPPORTED", -3: "H3_EALIGN", -
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh3qk.so")
 
 # every function include/h3qk.h declares
-EXPORTS = ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_last_error",
-           "h3_abi_version")
+EXPORTS = ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_swiglu",
+           "h3_scaled_residual", "h3_last_error", "h3_abi_version")
 
 
 class H3Error(RuntimeError):
@@ -65,7 +66,9 @@ def lib():
         L.h3_qk_rmsnorm_rope_permute.argtypes = [D, vp, i32, vp, vp, vp, i32, vp, i32, vp, vp]
         L.h3_qk_amax.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.h3_qk_cast_e4m3.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
-        for f in ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3"):
+        L.h3_swiglu.argtypes = [vp, i32, vp, ctypes.c_int64, ctypes.c_int64, vp]
+        L.h3_scaled_residual.argtypes = [vp, vp, i32, vp, ctypes.c_int64, vp, ctypes.c_int64, ctypes.c_int64, vp]
+        for f in ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_swiglu", "h3_scaled_residual"):
             getattr(L, f).restype = i32
         L.h3_last_error.restype = ctypes.c_char_p
         L.h3_last_error.argtypes = []
@@ -144,6 +147,17 @@ def h3_qk_cast_e4m3(desc: QkDesc, qkv, in_dt, w_q, w_k, amax_qk, q_codes, k_code
                                _ptr(amax_qk), _ptr(q_codes), _ptr(k_codes), _ptr(v_out), _ptr(descale_qk),
                                _stream(stream))
     _check("h3_qk_cast_e4m3", rc)
+
+
+def h3_swiglu(x, dt, y, N: int, F: int, stream=None) -> None:
+    rc = lib().h3_swiglu(_ptr(x), _dt(dt), _ptr(y), int(N), int(F), _stream(stream))
+    _check("h3_swiglu", rc)
+
+
+def h3_scaled_residual(res, branch, branch_dt, scale, scale_len: int, out, N: int, C: int, stream=None) -> None:
+    rc = lib().h3_scaled_residual(_ptr(res), _ptr(branch), _dt(branch_dt), _ptr(scale), int(scale_len), _ptr(out),
+                                  int(N), int(C), _stream(stream))
+    _check("h3_scaled_residual", rc)
 
 
 def h3_last_error() -> str:

@@ -47,6 +47,7 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
         return fail(H3_EUNSUPPORTED, "pairs_per_axis n must satisfy 0 <= 6n <= D");
     if (!std::isfinite(d->eps) || d->eps < 0.0f) return fail(H3_EINVAL, "eps must be finite and >= 0");
     if (d->row_stride < 3 * H * D) return fail(H3_EINVAL, "row_stride must be >= 3*H*D");
+    if (d->row_stride > ((int64_t)1 << 26)) return fail(H3_EINVAL, "row_stride must be <= 2^26 elements");
     if (B > 1 && d->batch_stride < T * d->row_stride) return fail(H3_EINVAL, "batch_stride must be >= T*row_stride");
     if (d->batch_stride < 0) return fail(H3_EINVAL, "batch_stride must be >= 0");
     if ((d->row_stride & 7) || (d->batch_stride & 7))
@@ -214,6 +215,49 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, con
     p.v = v_out;
     p.descale = descale_qk;
     return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
+int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream) {
+    if (!x || !y) return fail(H3_EINVAL, "x and y must be non-NULL");
+    if (dt != H3_F16 && dt != H3_BF16) return fail(H3_EUNSUPPORTED, "dt must be H3_F16 or H3_BF16");
+    if (N < 1 || F < 1) return fail(H3_EINVAL, "N and F must be >= 1");
+    if (F % 8) return fail(H3_EUNSUPPORTED, "F must be a multiple of 8");
+    if (N * F / 8 >= ((int64_t)1 << 32) || F > ((int64_t)1 << 30)) return fail(H3_EINVAL, "problem too large");
+    if (!aligned16(x) || !aligned16(y)) return fail(H3_EALIGN, "x and y must be 16-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), o = reinterpret_cast<uintptr_t>(y);
+    if (overlaps({o, o + (uintptr_t)(N * F * 2), "y"}, {a, a + (uintptr_t)(N * F * 4), "x"}))
+        return fail(H3_EALIAS, "y overlaps x");
+    std::string err;
+    const int rc = h3::launch_swiglu(dt, x, y, N, F, stream, &err);
+    if (rc != H3_OK) return fail(rc, err);
+    g_err.clear();
+    return H3_OK;
+}
+
+int h3_scaled_residual(const float *res, const void *branch, h3_dtype branch_dt, const float *scale,
+                       int64_t scale_len, float *out, int64_t N, int64_t C, hipStream_t stream) {
+    if (!res || !branch || !scale || !out) return fail(H3_EINVAL, "res, branch, scale and out must be non-NULL");
+    if (branch_dt != H3_F16 && branch_dt != H3_BF16) return fail(H3_EUNSUPPORTED, "branch_dt must be H3_F16 or H3_BF16");
+    if (N < 1 || C < 1) return fail(H3_EINVAL, "N and C must be >= 1");
+    if (C % 4) return fail(H3_EUNSUPPORTED, "C must be a multiple of 4");
+    if (scale_len != 1 && scale_len != C) return fail(H3_EINVAL, "scale_len must be 1 or C");
+    if (N * C / 4 >= ((int64_t)1 << 32) || C > ((int64_t)1 << 30)) return fail(H3_EINVAL, "problem too large");
+    if (!aligned16(res) || !aligned16(out) || (scale_len != 1 && !aligned16(scale)) ||
+        (reinterpret_cast<uintptr_t>(branch) & 7u) || (reinterpret_cast<uintptr_t>(scale) & 3u))
+        return fail(H3_EALIGN, "res, out (and a per-channel scale) must be 16-byte aligned, branch 8-byte");
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out);
+    const Range ro = {o, o + (uintptr_t)(N * C * 4), "out"};
+    const uintptr_t r = reinterpret_cast<uintptr_t>(res), b = reinterpret_cast<uintptr_t>(branch);
+    const uintptr_t sc = reinterpret_cast<uintptr_t>(scale);
+    const Range ins[] = {{r, r + (uintptr_t)(N * C * 4), "res"}, {b, b + (uintptr_t)(N * C * 2), "branch"},
+                         {sc, sc + (uintptr_t)(scale_len * 4), "scale"}};
+    for (const Range &in : ins)
+        if (overlaps(ro, in)) return fail(H3_EALIAS, std::string("out overlaps ") + in.name);
+    std::string err;
+    const int rc = h3::launch_scaled_residual(branch_dt, res, branch, scale, scale_len, out, N, C, stream, &err);
+    if (rc != H3_OK) return fail(rc, err);
+    g_err.clear();
+    return H3_OK;
 }
 
 const char *h3_last_error(void) { return g_err.c_str(); }

@@ -78,6 +78,11 @@ struct QkParams {
 // Launch one QK pass.  Returns H3_OK or H3_ELAUNCH / H3_EUNSUPPORTED with *err filled.
 int launch_qk(int mode, int D, int in_dt, int q_dt, int k_dt, QkParams &p, hipStream_t stream,
               std::string *err);
+
+// Decoder-block elementwise ops (arguments already validated).
+int launch_swiglu(int dt, const void *x, void *y, int64_t N, int64_t F, hipStream_t stream, std::string *err);
+int launch_scaled_residual(int dt, const float *res, const void *branch, const float *scale, int64_t scale_len,
+                           float *out, int64_t N, int64_t C, hipStream_t stream, std::string *err);
 #endif
 
 }  // namespace h3

@@ -222,14 +222,13 @@ constexpr bool kPairStore = M == 2 && (OT == DT_F16 || OT == DT_BF16) && W == 4;
 
 // ------------------------------------------------------------------ the row
 
-// One Q or K head row held as x[m][k] (dim 8W m + W ch + k, ch the lane's chunk): RMS normalisation with
-// weight w, then the rotation of the lane's pairs.  Binary32, one rounding per operation, the
-// halving reduction tree of the contract, no contraction (built with -ffp-contract=off).
+// One Q or K head row is held as x[m][k] (dim 8W m + W c + k, c the lane's chunk).  Binary32,
+// one rounding per operation, the halving reduction tree of the contract, no contraction (built
+// with -ffp-contract=off).
+
+// Sum of squares of the row over the halving tree; every lane of the token ends with it.
 template <int W, int M>
-__device__ __forceinline__ void norm_rope_row(float (&x)[M][W], const float (&w)[M][W], float eps,
-                                              float inv_d, const float (&cs)[M][W / 2],
-                                              const float (&sn)[M][W / 2],
-                                              const bool (&rot)[M][W / 2]) {
+__device__ __forceinline__ float row_sumsq(const float (&x)[M][W]) {
     float a[M][W];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -254,10 +253,22 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[M][W], const float (&w)
     for (int o = W / 2; o >= 1; o /= 2)
 #pragma unroll
         for (int k = 0; k < o; ++k) a[0][k] = a[0][k] + a[0][k + o];
-    const float ms = a[0][0] * inv_d;
+    return a[0][0];
+}
+
+// r = 1 / sqrt(ss * (1/D) + eps): correctly rounded sqrt, then correctly rounded division.
+__device__ __forceinline__ float row_rstd(float ss, float inv_d, float eps) {
+    const float ms = ss * inv_d;
     const float v = ms + eps;
-    const float sq = __builtin_sqrtf(v);  // correctly rounded
-    const float r = 1.0f / sq;            // correctly rounded
+    const float sq = __builtin_sqrtf(v);
+    return 1.0f / sq;
+}
+
+// y = (x r) w, then the rotation of the lane's pairs.
+template <int W, int M>
+__device__ __forceinline__ void row_scale_rotate(float (&x)[M][W], float r, const float (&w)[M][W],
+                                                 const float (&cs)[M][W / 2], const float (&sn)[M][W / 2],
+                                                 const bool (&rot)[M][W / 2]) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -276,6 +287,28 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[M][W], const float (&w)
             x[m][2 * q] = rot[m][q] ? e2 : e;
             x[m][2 * q + 1] = rot[m][q] ? f2 : f;
         }
+}
+
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {  // DPP quad_perm [J,J,J,J]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), J * 0x55, 0xF, 0xF, true));
+}
+
+// The 1/rms of up to 4 rows of a token with one square root and one division per lane: lane l of
+// each quad takes row l, and a DPP quad broadcast hands row j's value to every lane.  The 8 lanes
+// of a token are two quads, and both compute the same rows.
+template <int R>
+__device__ __forceinline__ void rows_rstd(const float (&ss)[R], int lane, float inv_d, float eps, float (&r)[R]) {
+    static_assert(R >= 1 && R <= 4, "one quad");
+    const int lr = lane & 3;
+    float mine = ss[0];
+#pragma unroll
+    for (int j = 1; j < R; ++j) mine = lr == j ? ss[j] : mine;
+    const float rm = row_rstd(mine, inv_d, eps);
+    r[0] = quad_bcast<0>(rm);
+    if constexpr (R > 1) r[1] = quad_bcast<1>(rm);
+    if constexpr (R > 2) r[2] = quad_bcast<2>(rm);
+    if constexpr (R > 3) r[3] = quad_bcast<3>(rm);
 }
 
 template <int W, int M, int IN>
@@ -410,43 +443,54 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     if (i >= p.T) return;  // ragged tail: the token's 8 lanes leave together
     const int h0 = hc * HPW;
     const int nh = min(HPW, p.H - h0);
+    // Uniform bases (the wave's first token, head h0) and small per-lane offsets, so memory
+    // instructions take a scalar base with a 32-bit lane offset.
     const int64_t plane = (int64_t)p.T * D;
-    const int64_t orow = (((int64_t)b * p.H + h0) * p.T + i) * D;  // element of (b, h0, i, 0)
+    const int64_t obase = (((int64_t)b * p.H + h0) * p.T + (int64_t)tg * 8) * D;  // (b, h0, 8 tg, 0)
+    const uint32_t olane = (uint32_t)g * D;
 
     if (i >= p.vlen[b]) {  // padding token: +0 everywhere
 #pragma unroll
         for (int u = 0; u < HPW; ++u) {
             if (u >= nh) break;
-            const int64_t o = orow + u * plane;
+            const int64_t o = obase + u * plane;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                store_zero_chunk<QT, W>(p.q, o + 8 * W * m + W * c);
-                store_zero_chunk<KT, W>(p.k, o + 8 * W * m + W * c);
+                store_zero_chunk<QT, W>(p.q, o + (olane + 8 * W * m + W * c));
+                store_zero_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c));
             }
 #pragma unroll
             for (int vc = 0; vc < VC; ++vc)
-                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + 64 * vc + 8 * c),
+                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)),
                       (u32x4){0u, 0u, 0u, 0u});
         }
         return;
     }
 
     // 1. every data load of the item, before anything that depends on them
-    const uint16_t *tok = p.qkv + (int64_t)b * p.batch_stride + (int64_t)i * p.row_stride;
+    const uint16_t *tokb = p.qkv + (int64_t)b * p.batch_stride + (int64_t)tg * 8 * p.row_stride;
+    const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
     uint32_t rq[HPW][M][W / 2], rk[HPW][M][W / 2];
     u32x4 rv[HPW][VC];
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        if (u >= nh) break;
-        const int h = h0 + u;
+        if (u < nh) {
+            const uint32_t hq = (uint32_t)(h0 + u) * D, hk = (uint32_t)(p.H + h0 + u) * D;
+            const uint32_t hv = (uint32_t)(2 * p.H + h0 + u) * D;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, rq[u][m]);
-            load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, rk[u][m]);
+            for (int m = 0; m < M; ++m) {
+                load_chunk<W>(tokb + (tlane + hq + 8 * W * m + W * c), rq[u][m]);
+                load_chunk<W>(tokb + (tlane + hk + 8 * W * m + W * c), rk[u][m]);
+            }
+#pragma unroll
+            for (int vc = 0; vc < VC; ++vc)
+                rv[u][vc] = *reinterpret_cast<const u32x4 *>(tokb + (tlane + hv + 64 * vc + 8 * c));
+        } else {  // absent head of an odd head count: zeros (their rows are never stored)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int k = 0; k < W / 2; ++k) rq[u][m][k] = rk[u][m][k] = 0u;
         }
-#pragma unroll
-        for (int vc = 0; vc < VC; ++vc)
-            rv[u][vc] = *reinterpret_cast<const u32x4 *>(tok + (int64_t)(2 * p.H + h) * D + 64 * vc + 8 * c);
     }
     // 2. weights and rotary entries while the loads are in flight
     float wq[M][W], wk[M][W];
@@ -457,16 +501,35 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     rotary_entries<W, M, NN>(p, b, i, c, cs, sn, rot);
     const float inv_d = 1.0f / (float)D;
 
-    // 3. normalise, rotate, store
+    // 3. sums of squares of the 2 HPW rows and their 1/rms.  The ALU-bound cast shares one square
+    // root and division per lane among the rows; the store pass keeps one per row, whose
+    // independent chains hide latency better at 3 waves per SIMD (measured: shared is 7 % slower
+    // on the full latent, 35 % on one tile).
+    float x[HPW][2][M][W];
+    float ss[2 * HPW], rr[2 * HPW];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+        unpack_row<W, M, IN>(rq[u], x[u][0]);
+        unpack_row<W, M, IN>(rk[u], x[u][1]);
+        ss[2 * u] = row_sumsq<W, M>(x[u][0]);
+        ss[2 * u + 1] = row_sumsq<W, M>(x[u][1]);
+    }
+    if constexpr (MODE == MODE_CAST) {
+        rows_rstd<2 * HPW>(ss, lane, inv_d, p.eps, rr);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2 * HPW; ++j) rr[j] = row_rstd(ss[j], inv_d, p.eps);
+    }
+
+    // 4. normalise, rotate, store
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
         if (u >= nh) break;
-        const int64_t o = orow + u * plane;
-        float xq[M][W], xk[M][W];
-        unpack_row<W, M, IN>(rq[u], xq);
-        unpack_row<W, M, IN>(rk[u], xk);
-        norm_rope_row<W, M>(xq, wq, p.eps, inv_d, cs, sn, rot);
-        norm_rope_row<W, M>(xk, wk, p.eps, inv_d, cs, sn, rot);
+        const int64_t o = obase + u * plane;
+        float (&xq)[M][W] = x[u][0];
+        float (&xk)[M][W] = x[u][1];
+        row_scale_rotate<W, M>(xq, rr[2 * u], wq, cs, sn, rot);
+        row_scale_rotate<W, M>(xk, rr[2 * u + 1], wk, cs, sn, rot);
         if constexpr (MODE == MODE_CAST) {
             float qq[2][M][W];
             bool bad = false;  // a quotient above 448 in magnitude or NaN
@@ -496,32 +559,32 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 pack_e4m3<W>(qq[1][m], !exact, cw[1][m]);
             }
             if constexpr (W == 8 && M == 2) {
-                store_words_pairs<1, W>(p.q, o, c, cw[0][0], cw[0][1]);
-                store_words_pairs<1, W>(p.k, o, c, cw[1][0], cw[1][1]);
+                store_words_pairs<1, W>(p.q, o + olane, c, cw[0][0], cw[0][1]);
+                store_words_pairs<1, W>(p.k, o + olane, c, cw[1][0], cw[1][1]);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    store_code_words<W>(p.q, o + 8 * W * m + W * c, cw[0][m]);
-                    store_code_words<W>(p.k, o + 8 * W * m + W * c, cw[1][m]);
+                    store_code_words<W>(p.q, o + (olane + 8 * W * m + W * c), cw[0][m]);
+                    store_code_words<W>(p.k, o + (olane + 8 * W * m + W * c), cw[1][m]);
                 }
             }
         } else {
             if constexpr (kPairStore<QT, W, M>) {
-                store_row_pairs<QT, W>(p.q, o, c, xq);
+                store_row_pairs<QT, W>(p.q, o + olane, c, xq);
             } else {
 #pragma unroll
-                for (int m = 0; m < M; ++m) store_chunk<QT, W>(p.q, o + 8 * W * m + W * c, xq[m]);
+                for (int m = 0; m < M; ++m) store_chunk<QT, W>(p.q, o + (olane + 8 * W * m + W * c), xq[m]);
             }
             if constexpr (kPairStore<KT, W, M>) {
-                store_row_pairs<KT, W>(p.k, o, c, xk);
+                store_row_pairs<KT, W>(p.k, o + olane, c, xk);
             } else {
 #pragma unroll
-                for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + 8 * W * m + W * c, xk[m]);
+                for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c), xk[m]);
             }
         }
 #pragma unroll
         for (int vc = 0; vc < VC; ++vc)
-            st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + 64 * vc + 8 * c), rv[u][vc]);
+            st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)), rv[u][vc]);
     }
 }
 
@@ -558,12 +621,16 @@ __device__ __forceinline__ void amax_fetch(const QkParams &p, int64_t item, int 
     const uint16_t *tok = p.qkv + (int64_t)it.b * p.batch_stride + (int64_t)it.i * p.row_stride;
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        if (u >= it.nh) break;
         const int h = it.h0 + u;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, it.rq[u][m]);
-            load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, it.rk[u][m]);
+            if (u < it.nh) {
+                load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, it.rq[u][m]);
+                load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, it.rk[u][m]);
+            } else {  // absent head of an odd head count: zeros, never reduced
+#pragma unroll
+                for (int k = 0; k < W / 2; ++k) it.rq[u][m][k] = it.rk[u][m][k] = 0u;
+            }
         }
     }
 }
@@ -601,8 +668,10 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
                 float xq[M][W], xk[M][W];
                 unpack_row<W, M, IN>(cur.rq[u], xq);
                 unpack_row<W, M, IN>(cur.rk[u], xk);
-                norm_rope_row<W, M>(xq, wq, p.eps, inv_d, cs, sn, rot);
-                norm_rope_row<W, M>(xk, wk, p.eps, inv_d, cs, sn, rot);
+                const float rq_ = row_rstd(row_sumsq<W, M>(xq), inv_d, p.eps);
+                const float rk_ = row_rstd(row_sumsq<W, M>(xk), inv_d, p.eps);
+                row_scale_rotate<W, M>(xq, rq_, wq, cs, sn, rot);
+                row_scale_rotate<W, M>(xk, rk_, wk, cs, sn, rot);
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll

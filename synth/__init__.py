@@ -261,3 +261,37 @@ def qkv_device(wl: Workload, device="cuda"):
     caller as float16 / bfloat16)."""
     v = values_torch(wl.seed, S_QKV, 0, wl.qkv_numel(), wl.dist, wl.in_dtype, device)
     return v.view(wl.B, wl.T, wl.stride)
+
+
+# ----------------------------------------------------------------------------- decoder-block ops
+
+S_SWIGLU, S_RES, S_BRANCH, S_SCALE = 5, 6, 7, 8
+
+# Shapes of the isolated decoder-block measurements of the vllm-omni MiniMax-H3 VAE review thread:
+# SwiGLU on the w1 output [1, 1797, 16384]; scaled residual on [2, 1797, 2048].
+SWIGLU_SHAPE = (1797, 8192)          # (N, F): x is [N, 2F]
+RESIDUAL_SHAPE = (2 * 1797, 2048)    # (N, C)
+
+
+def swiglu_input(N: int, F: int, dtype: str = "f16", seed: int = 2000) -> np.ndarray:
+    """uint16 bits [N, 2F]: standard normal x 3 (so the gate spans silu's curved region)."""
+    idx = np.arange(N * 2 * F, dtype=np.int64)
+    q = normal_quantiles()
+    h = hash_np(seed, S_SWIGLU, idx)
+    v = (3.0 * q)[(h >> np.uint64(48)).astype(np.int64)]
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16).reshape(N, 2 * F)
+    return _f32_to_bf16_bits(v.astype(np.float32)).reshape(N, 2 * F)
+
+
+def residual_inputs(N: int, C: int, dtype: str = "f16", seed: int = 2001):
+    """(res fp32 [N, C], branch 16-bit bits [N, C], scale fp32 [C] = 1 + 0.1 z)."""
+    q = normal_quantiles()
+    idx = np.arange(N * C, dtype=np.int64)
+    res = q[(hash_np(seed, S_RES, idx) >> np.uint64(48)).astype(np.int64)].astype(np.float32).reshape(N, C)
+    braw = q[(hash_np(seed, S_BRANCH, idx) >> np.uint64(48)).astype(np.int64)]
+    branch = (braw.astype(np.float16).view(np.uint16) if dtype == "f16"
+              else _f32_to_bf16_bits(braw.astype(np.float32))).reshape(N, C)
+    sc = q[(hash_np(seed, S_SCALE, np.arange(C)) >> np.uint64(48)).astype(np.int64)]
+    scale = (1.0 + 0.1 * sc).astype(np.float32)
+    return res, branch, scale

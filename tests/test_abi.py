@@ -130,3 +130,34 @@ def test_amax_and_cast_validation():
 def test_null_descriptor():
     rc = h3.lib().h3_qk_rmsnorm_rope_permute(None, BASE, 1, BASE, BASE, BASE, 0, BASE, 1, BASE, None)
     assert rc == -1 and "desc" in h3.h3_last_error()
+
+
+def test_block_op_validation():
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_swiglu(BASE, h3.F16, BASE + 0x40000000, 4, 12, stream=0)
+    assert e.value.name == "H3_EUNSUPPORTED"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_swiglu(BASE, h3.F16, BASE + 64, 4, 16, stream=0)       # y inside x
+    assert e.value.name == "H3_EALIAS"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_swiglu(BASE + 8, h3.F16, BASE + 0x40000000, 4, 16, stream=0)
+    assert e.value.name == "H3_EALIGN"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_swiglu(BASE, h3.F32, BASE + 0x40000000, 4, 16, stream=0)
+    assert e.value.name == "H3_EUNSUPPORTED"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_swiglu(0, h3.F16, BASE + 0x40000000, 4, 16, stream=0)
+    assert e.value.name == "H3_EINVAL"
+    R, Bq, S, O = BASE, BASE + 0x10000000, BASE + 0x20000000, BASE + 0x30000000
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_scaled_residual(R, Bq, h3.F16, S, 3, O, 4, 8, stream=0)     # scale_len not 1 or C
+    assert e.value.name == "H3_EINVAL"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_scaled_residual(R, Bq, h3.F16, S, 1, O, 4, 6, stream=0)     # C not a multiple of 4
+    assert e.value.name == "H3_EUNSUPPORTED"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_scaled_residual(R, Bq, h3.F16, S, 1, R + 16, 4, 8, stream=0)  # out overlaps res
+    assert e.value.name == "H3_EALIAS"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_scaled_residual(R, Bq + 4, h3.F16, S, 8, O, 4, 8, stream=0)
+    assert e.value.name == "H3_EALIGN"
