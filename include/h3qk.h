@@ -139,10 +139,10 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
  * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,
  * SwiGLU row: SiluAndMul after the FP16 w1 output):
  *   x  DEVICE dt [N][2F] row-major: gate g = x[:, :F], up u = x[:, F:]
- *   y  DEVICE dt [N][F]:  y = RN_dt( (g / (1 + exp(-g))) * u ), every step in binary32
+ *   y  DEVICE dt [N][F]:  y = RN_dt( (g / (1 + exp(-g))) * u ), evaluated in binary32
  * dt is H3_F16 or H3_BF16; F a multiple of 8; N * F / 8 < 2^32; x, y 16-byte aligned, not
- * overlapping.  exp is the device library's binary32 exp (about 1 ulp), so y may differ by one
- * ulp of dt from the exactly rounded value.
+ * overlapping.  exp and the reciprocal are the hardware binary32 approximations (relative error
+ * below 1e-6), so y may sit one ulp of dt from the exactly rounded value.
  */
 int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream);
 

@@ -3,8 +3,9 @@
 //   SwiGLU          y = silu(g) u on the 16-bit w1 output [N, 2F] (g = first F columns, u = the rest),
 //                   computed in binary32 with the device exp, rounded once to the 16-bit output;
 //   scaled residual out = res + (branch * scale) in binary32, product rounded first (no contraction).
-// Both stream with no reuse: one 16-byte vector per lane and short-lived 256-thread blocks that
-// sweep the tensors in order; outputs bypass the caches (nontemporal stores).
+// Both stream with no reuse: 16-byte vectors, two per lane (the second 256 vectors after the first),
+// short-lived 256-thread blocks that sweep the tensors in order; outputs bypass the caches
+// (nontemporal stores).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,6 +17,8 @@ namespace {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kVectorsPerThread = 2;
 
 template <int DT>
 __device__ __forceinline__ float h16_to_f32(uint32_t b) {
@@ -29,19 +32,22 @@ __device__ __forceinline__ uint32_t f32_to_h16(float x) {
     else return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// silu(g) u = (g / (1 + exp(-g))) u: every operation rounded in binary32 (exp from the device math
-// library, about 1 ulp; the division correctly rounded).
+// silu(g) u = (g / (1 + exp(-g))) u in binary32 with the hardware exp2 and reciprocal: a few
+// binary32 ulps in all (relative error below 1e-6), far under one ulp of the 16-bit output, so the
+// rounded result is the exactly rounded one except next to a rounding boundary, where it may be one
+// 16-bit ulp away.  exp(-g) overflows to +inf for g below about -88, giving silu = -0.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    const float e = __builtin_expf(-g);
+    const float e = __expf(-g);
     const float d = 1.0f + e;
-    const float s = g / d;
+    const float s = g * __builtin_amdgcn_rcpf(d);
     return s * u;
 }
 
 template <int DT>
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ y,
                                                      uint32_t vectors, DivMagic f8, uint32_t F) {
-    const uint32_t t = blockIdx.x * 256u + threadIdx.x;  // one 8-element output vector
+  for (int v = 0; v < kVectorsPerThread; ++v) {
+    const uint32_t t = blockIdx.x * (256u * kVectorsPerThread) + v * 256u + threadIdx.x;  // 8 outputs
     if (t >= vectors) return;
     const uint32_t n = div_apply(t, f8);                  // row
     const uint32_t f = (t - n * f8.d) * 8u;               // column of the first output
@@ -57,6 +63,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *__restrict_
     }
     __builtin_nontemporal_store((u32x4){o[0], o[1], o[2], o[3]},
                                 reinterpret_cast<u32x4 *>(y + (uint64_t)t * 8u));
+  }
 }
 
 template <int DT, bool PER_CHANNEL>
@@ -65,7 +72,8 @@ __global__ __launch_bounds__(256) void scaled_residual_kernel(const float *__res
                                                               const float *__restrict__ scale,
                                                               float *__restrict__ out, uint32_t vectors,
                                                               DivMagic c4) {
-    const uint32_t t = blockIdx.x * 256u + threadIdx.x;  // one 4-element vector
+  for (int v = 0; v < kVectorsPerThread; ++v) {
+    const uint32_t t = blockIdx.x * (256u * kVectorsPerThread) + v * 256u + threadIdx.x;  // 4 elements
     if (t >= vectors) return;
     const f32x4 r = *reinterpret_cast<const f32x4 *>(res + (uint64_t)t * 4u);
     const u32x2 b = *reinterpret_cast<const u32x2 *>(br + (uint64_t)t * 4u);
@@ -81,10 +89,11 @@ __global__ __launch_bounds__(256) void scaled_residual_kernel(const float *__res
     const float p0 = b0 * s.x, p1 = b1 * s.y, p2 = b2 * s.z, p3 = b3 * s.w;
     __builtin_nontemporal_store((f32x4){r.x + p0, r.y + p1, r.z + p2, r.w + p3},
                                 reinterpret_cast<f32x4 *>(out + (uint64_t)t * 4u));
+  }
 }
 
 int launch(const void *kern, uint32_t vectors, void **args, hipStream_t stream, std::string *err) {
-    const uint32_t blocks = (vectors + 255u) / 256u;
+    const uint32_t blocks = (vectors + 256u * kVectorsPerThread - 1u) / (256u * kVectorsPerThread);
     if (blocks == 0) return H3_OK;
     const hipError_t e = hipLaunchKernel(kern, dim3(blocks), dim3(256), args, 0, stream);
     if (e != hipSuccess) {
