@@ -50,6 +50,11 @@ def lib():
         L.h3ref_qk_cast_e4m3.argtypes = [P, vp, ctypes.c_int, fp, fp, fp, vp, vp, vp, fp]
         L.h3ref_qk_tokens.argtypes = [P, vp, ctypes.c_int, fp, fp, vp, i64, ctypes.c_int, fp, vp,
                                       ctypes.c_int, vp, ctypes.c_int, vp, fp]
+        L.h3ref_qk_cast_e4m3_static.argtypes = [P, vp, ctypes.c_int, fp, fp, fp, ctypes.c_int, vp, vp, vp, vp]
+        L.h3ref_qk_tokens_ex.argtypes = [P, vp, ctypes.c_int, fp, fp, vp, i64, ctypes.c_int, fp, ctypes.c_int,
+                                         vp, ctypes.c_int, vp, ctypes.c_int, vp, fp, vp]
+        L.h3ref_static_descale.argtypes = [ctypes.c_float]
+        L.h3ref_static_descale.restype = ctypes.c_float
         L.h3ref_norm_rope_row.argtypes = [fp, ctypes.c_int, fp, ctypes.c_float, ctypes.c_int, vp, vp, fp]
         L.h3ref_token_rows.argtypes = [P, ctypes.c_int, i64, vp]
         for n in ("f16", "bf16"):
@@ -177,22 +182,60 @@ def qk_cast_e4m3(spec: Spec, qkv: np.ndarray, in_dt: str, w_q, w_k, amax):
     return q, k, v, ds
 
 
+def qk_cast_e4m3_static(spec: Spec, qkv: np.ndarray, in_dt: str, w_q, w_k, descale, v_fp8: bool = False):
+    """FP8 cast with caller descales ([2], or [3] with v_fp8).  Returns (q, k, v, sat) with sat the
+    uint64 [3] clip counts; v is uint8 codes when v_fp8, else the 16-bit bit copy."""
+    qkv = np.ascontiguousarray(qkv, dtype=np.uint16)
+    wq, wk = _f32(w_q), _f32(w_k)
+    ds = np.ones(3, np.float32)
+    d = _f32(descale).ravel()
+    ds[:d.size] = d
+    shape = (spec.B, spec.H, spec.T, spec.D)
+    q = np.empty(shape, np.uint8); k = np.empty(shape, np.uint8)
+    v = np.empty(shape, np.uint8 if v_fp8 else np.uint16)
+    sat = np.zeros(3, np.uint64)
+    P = spec.c()
+    rc = lib().h3ref_qk_cast_e4m3_static(ctypes.byref(P), _ptr(qkv), DT[in_dt], _ptr(wq), _ptr(wk), _ptr(ds),
+                                         int(v_fp8), _ptr(q), _ptr(k), _ptr(v), _ptr(sat))
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return q, k, v, sat
+
+
+def static_descale(d: float) -> float:
+    return lib().h3ref_static_descale(ctypes.c_float(d))
+
+
 def qk_tokens(spec: Spec, qkv_rows: np.ndarray, tokens, in_dt: str, w_q, w_k, q_dt="f32", k_dt="f16",
-              fp8=False, amax=None):
+              fp8=False, amax=None, descale=None, v_fp8=False, sat=None):
     """Outputs for selected tokens only.  qkv_rows [n_tok, row_stride] holds their input rows.
-    Returns (q, k, v, y) with q, k, v [n_tok, H, D] and y the f32 y' [n_tok, 2, H, D]."""
+    fp8: descales from amax (dynamic) or, when `descale` is given, the caller's static descales
+    (guarded like the library); v_fp8 casts V with descale[2].  Returns (q, k, v, y) with q, k, v
+    [n_tok, H, D] and y the f32 y' [n_tok, 2, H, D]; `sat` (uint64 [3]) is added to."""
     tokens = np.ascontiguousarray(tokens, dtype=np.int64)
     n = tokens.size
     rows = np.ascontiguousarray(qkv_rows, dtype=np.uint16).reshape(n, spec.row_stride)
     wq, wk = _f32(w_q), _f32(w_k)
-    am = _f32(np.zeros(2) if amax is None else amax)
+    ds = np.ones(3, np.float32)
+    if fp8 and descale is not None:
+        d = _f32(descale).ravel()
+        for j in range(d.size):
+            ds[j] = static_descale(float(d[j]))
+    elif fp8:
+        am = _f32(np.zeros(2) if amax is None else amax).ravel()
+        for j in range(am.size):
+            ds[j] = descale_of(float(am[j]))
     qd, kd = ("e4m3", "e4m3") if fp8 else (q_dt, k_dt)
     shape = (n, spec.H, spec.D)
-    q = np.empty(shape, NP_DT[qd]); k = np.empty(shape, NP_DT[kd]); v = np.empty(shape, np.uint16)
+    q = np.empty(shape, NP_DT[qd]); k = np.empty(shape, NP_DT[kd])
+    v = np.empty(shape, np.uint8 if (fp8 and v_fp8) else np.uint16)
     y = np.empty((n, 2, spec.H, spec.D), np.float32)
+    counts = np.zeros(3, np.uint64) if sat is None else sat
+    assert counts.dtype == np.uint64 and counts.size == 3 and counts.flags.c_contiguous
     P = spec.c()
-    rc = lib().h3ref_qk_tokens(ctypes.byref(P), _ptr(rows), DT[in_dt], _ptr(wq), _ptr(wk), _ptr(tokens), n,
-                               int(fp8), _ptr(am), _ptr(q), DT[qd], _ptr(k), DT[kd], _ptr(v), _ptr(y))
+    rc = lib().h3ref_qk_tokens_ex(ctypes.byref(P), _ptr(rows), DT[in_dt], _ptr(wq), _ptr(wk), _ptr(tokens), n,
+                                  int(fp8), _ptr(ds), int(v_fp8), _ptr(q), DT[qd], _ptr(k), DT[kd], _ptr(v), _ptr(y),
+                                  _ptr(counts))
     if rc:
         raise ValueError(f"oracle: position outside the tables (rc={rc})")
     return q, k, v, y
@@ -237,6 +280,9 @@ def decode(bits: np.ndarray, dt: str) -> np.ndarray:
 
 def descale(amax: float) -> float:
     return lib().h3ref_descale(ctypes.c_float(amax))
+
+
+descale_of = descale
 
 
 def swiglu(x_bits: np.ndarray, in_dt: str = "f16") -> np.ndarray:

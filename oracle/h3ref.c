@@ -227,46 +227,67 @@ static int token_qk(const h3ref_problem *P, const uint16_t *row, int in_dt, cons
 }
 
 /*
- * Store one token.  Non-FP8 (fp8 == 0): Q and K take y' rounded to their dtypes.  FP8: Q and K
- * take E4M3(y' / descale[s]).  V is a bit copy of the 16-bit input.  A padded token is +0
- * everywhere.  Output element (h, d) of this token goes to index o0 + h * head_stride + d.
+ * What one store writes.  fp8 == 0: Q and K take y' rounded to q_dt / k_dt, V is a bit copy.
+ * fp8 == 1: Q and K take E4M3(y' / ds[s]); V takes E4M3(v / ds[2]) when v_fp8, else a bit copy.
+ * sat (optional) counts, per tensor (Q, K, V), the cast elements whose quotient lies outside the
+ * E4M3 range, |y' / ds| > 448 (TensorRT-LLM PR #21485, the saturation-log commit: elements clipped
+ * at the E4M3 range per tensor).  A NaN quotient is not counted; padded tokens are not counted.
  */
-static void store_token(const h3ref_problem *P, const uint16_t *row, int padded, const float *yqk,
-                        int fp8, const float *ds, void *q, int q_dt, void *k, int k_dt, void *v,
-                        int64_t o0, int64_t head_stride) {
+typedef struct {
+    int fp8, v_fp8;
+    float ds[3];
+    uint64_t *sat;
+} store_opts;
+
+static uint8_t cast_one(float t, float ds, uint64_t *sat) {
+    float q = t / ds;
+    if (sat && fabsf(q) > 448.0f) *sat += 1;
+    return h3ref_e4m3_encode(q);
+}
+
+/*
+ * Store one token.  A padded token is +0 everywhere.  Output element (h, d) of this token goes
+ * to index o0 + h * head_stride + d.
+ */
+static void store_token(const h3ref_problem *P, const uint16_t *row, int in_dt, int padded,
+                        const float *yqk, const store_opts *so, void *q, int q_dt, void *k, int k_dt,
+                        void *v, int64_t o0, int64_t head_stride) {
     int H = P->H, D = P->D;
     for (int h = 0; h < H; ++h) {
         int64_t o = o0 + (int64_t)h * head_stride;
         for (int s = 0; s < 2; ++s) {
             void *dst = s == 0 ? q : k;
-            int dt = fp8 ? REF_E4M3 : (s == 0 ? q_dt : k_dt);
+            int dt = so->fp8 ? REF_E4M3 : (s == 0 ? q_dt : k_dt);
             const float *y = yqk + ((int64_t)s * H + h) * D;
             for (int d = 0; d < D; ++d) {
                 if (padded) { memset((char *)dst + (o + d) * dt_size(dt), 0, (size_t)dt_size(dt)); continue; }
-                float t = y[d];
-                if (fp8) t = t / ds[s];
-                store_out(dst, dt, o + d, t);
+                if (so->fp8) ((uint8_t *)dst)[o + d] = cast_one(y[d], so->ds[s], so->sat ? so->sat + s : 0);
+                else store_out(dst, dt, o + d, y[d]);
             }
         }
-        for (int d = 0; d < D; ++d)
-            ((uint16_t *)v)[o + d] = padded ? 0 : row[((int64_t)2 * H + h) * D + d];
+        int64_t vi = ((int64_t)2 * H + h) * D;
+        for (int d = 0; d < D; ++d) {
+            if (so->fp8 && so->v_fp8)
+                ((uint8_t *)v)[o + d] = padded ? 0 : cast_one(load_in(row, in_dt, vi + d), so->ds[2],
+                                                              so->sat ? so->sat + 2 : 0);
+            else
+                ((uint16_t *)v)[o + d] = padded ? 0 : row[vi + d];
+        }
     }
 }
 
 /* descale = amax / 448 when amax > 0, else 1 (an all-zero or empty tensor). */
 float h3ref_descale(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
 
+/* A descale from a caller's table: used as given when > 0, else 1 (zero, negative or NaN), the
+   same guard as the dynamic descale. */
+float h3ref_static_descale(float d) { return d > 0.0f ? d : 1.0f; }
+
 static int run_items(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q,
-                     const float *w_k, int fp8, const float *amax, void *q, int q_dt, void *k,
-                     int k_dt, void *v, float *descale) {
+                     const float *w_k, const store_opts *so, void *q, int q_dt, void *k, int k_dt,
+                     void *v) {
     int H = P->H, D = P->D;
     int64_t plane = (int64_t)H * P->T * D;
-    float ds[2] = {1.0f, 1.0f};
-    if (fp8) {
-        ds[0] = h3ref_descale(amax[0]);
-        ds[1] = h3ref_descale(amax[1]);
-        if (descale) { descale[0] = ds[0]; descale[1] = ds[1]; }
-    }
     static float yqk[2 * 64 * 256];
     if (H > 64 || D > 256) return -2;
     for (int b = 0; b < P->B; ++b)
@@ -274,7 +295,7 @@ static int run_items(const h3ref_problem *P, const void *qkv, int in_dt, const f
             const uint16_t *row = (const uint16_t *)qkv + (int64_t)b * P->batch_stride + i * P->row_stride;
             int rc = token_qk(P, row, in_dt, w_q, w_k, b, i, yqk);
             if (rc < 0) return rc;
-            store_token(P, row, rc == 1, yqk, fp8, ds, q, q_dt, k, k_dt, v, b * plane + i * D,
+            store_token(P, row, in_dt, rc == 1, yqk, so, q, q_dt, k, k_dt, v, b * plane + i * D,
                         (int64_t)P->T * D);
         }
     return 0;
@@ -287,7 +308,8 @@ static int run_items(const h3ref_problem *P, const void *qkv, int in_dt, const f
 int h3ref_qk_rmsnorm_rope_permute(const h3ref_problem *P, const void *qkv, int in_dt,
                                   const float *w_q, const float *w_k,
                                   void *q, int q_dt, void *k, int k_dt, void *v) {
-    return run_items(P, qkv, in_dt, w_q, w_k, 0, 0, q, q_dt, k, k_dt, v, 0);
+    store_opts so = {0, 0, {1.0f, 1.0f, 1.0f}, 0};
+    return run_items(P, qkv, in_dt, w_q, w_k, &so, q, q_dt, k, k_dt, v);
 }
 
 /*
@@ -323,23 +345,45 @@ int h3ref_qk_amax(const h3ref_problem *P, const void *qkv, int in_dt, const floa
 int h3ref_qk_cast_e4m3(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q,
                        const float *w_k, const float amax[2], uint8_t *q, uint8_t *k, void *v,
                        float descale[2]) {
-    return run_items(P, qkv, in_dt, w_q, w_k, 1, amax, q, REF_E4M3, k, REF_E4M3, v, descale);
+    store_opts so = {1, 0, {h3ref_descale(amax[0]), h3ref_descale(amax[1]), 1.0f}, 0};
+    if (descale) { descale[0] = so.ds[0]; descale[1] = so.ds[1]; }
+    return run_items(P, qkv, in_dt, w_q, w_k, &so, q, REF_E4M3, k, REF_E4M3, v);
+}
+
+/*
+ * FP8 cast with static descales (TensorRT-LLM PR #21485: a static scale table as the opt-in
+ * alternative to the dynamic amax pass; the saturation-log commit).  descale[0], [1] (and [2]
+ * when v_fp8) come from the caller, each guarded by h3ref_static_descale.  Q and K codes are
+ * E4M3(y' / descale_s); V is E4M3(v / descale_2) when v_fp8, else a bit copy.  sat[3] (optional)
+ * is overwritten with the per-tensor counts of |quotient| > 448 (sat[2] = 0 when V is copied).
+ */
+int h3ref_qk_cast_e4m3_static(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q,
+                              const float *w_k, const float *descale, int v_fp8, uint8_t *q,
+                              uint8_t *k, void *v, uint64_t *sat) {
+    store_opts so = {1, v_fp8 ? 1 : 0,
+                     {h3ref_static_descale(descale[0]), h3ref_static_descale(descale[1]),
+                      v_fp8 ? h3ref_static_descale(descale[2]) : 1.0f},
+                     sat};
+    if (sat) { sat[0] = 0; sat[1] = 0; sat[2] = 0; }
+    return run_items(P, qkv, in_dt, w_q, w_k, &so, q, REF_E4M3, k, REF_E4M3, v);
 }
 
 /*
  * The same outputs for a list of tokens only (flat ids b * T + i), reading a compact input
  * qkv_rows [n_tok][row_stride] whose row t is token tokens[t].  Outputs are [n_tok][H][D].
- * fp8 == 0: Q, K in q_dt, k_dt (amax ignored).  fp8 == 1: E4M3 codes with descales from amax.
- * yf32 (optional) receives y' as f32 [n_tok][2][H][D] (zeros for padded tokens).
+ * fp8 == 0: Q, K in q_dt, k_dt (descale ignored).  fp8 == 1: E4M3 codes with the final descales
+ * descale[3] (V codes with descale[2] when v_fp8).  yf32 (optional) receives y' as f32
+ * [n_tok][2][H][D] (zeros for padded tokens); sat[3] (optional) is added to.
  */
-int h3ref_qk_tokens(const h3ref_problem *P, const void *qkv_rows, int in_dt, const float *w_q,
-                    const float *w_k, const int64_t *tokens, int64_t n_tok, int fp8,
-                    const float *amax, void *q, int q_dt, void *k, int k_dt, void *v, float *yf32) {
+int h3ref_qk_tokens_ex(const h3ref_problem *P, const void *qkv_rows, int in_dt, const float *w_q,
+                       const float *w_k, const int64_t *tokens, int64_t n_tok, int fp8,
+                       const float *descale, int v_fp8, void *q, int q_dt, void *k, int k_dt, void *v,
+                       float *yf32, uint64_t *sat) {
     static float yqk[2 * 64 * 256];
     int H = P->H, D = P->D;
     if (H > 64 || D > 256) return -2;
-    float ds[2] = {1.0f, 1.0f};
-    if (fp8) { ds[0] = h3ref_descale(amax[0]); ds[1] = h3ref_descale(amax[1]); }
+    store_opts so = {fp8 ? 1 : 0, fp8 && v_fp8 ? 1 : 0, {1.0f, 1.0f, 1.0f}, sat};
+    if (fp8) { so.ds[0] = descale[0]; so.ds[1] = descale[1]; if (v_fp8) so.ds[2] = descale[2]; }
     for (int64_t t = 0; t < n_tok; ++t) {
         int b = (int)(tokens[t] / P->T);
         int64_t i = tokens[t] % P->T;
@@ -348,10 +392,20 @@ int h3ref_qk_tokens(const h3ref_problem *P, const void *qkv_rows, int in_dt, con
         if (rc < 0) return rc;
         if (rc == 1) memset(yqk, 0, sizeof(float) * 2 * H * D);
         if (yf32) memcpy(yf32 + t * 2 * H * D, yqk, sizeof(float) * 2 * H * D);
-        store_token(P, row, rc == 1, yqk, fp8, ds, q, fp8 ? REF_E4M3 : q_dt, k,
+        store_token(P, row, in_dt, rc == 1, yqk, &so, q, fp8 ? REF_E4M3 : q_dt, k,
                     fp8 ? REF_E4M3 : k_dt, v, t * H * D, D);
     }
     return 0;
+}
+
+/* h3ref_qk_tokens_ex with descales from amax (fp8 == 1) and V copied. */
+int h3ref_qk_tokens(const h3ref_problem *P, const void *qkv_rows, int in_dt, const float *w_q,
+                    const float *w_k, const int64_t *tokens, int64_t n_tok, int fp8,
+                    const float *amax, void *q, int q_dt, void *k, int k_dt, void *v, float *yf32) {
+    float ds[3] = {1.0f, 1.0f, 1.0f};
+    if (fp8) { ds[0] = h3ref_descale(amax[0]); ds[1] = h3ref_descale(amax[1]); }
+    return h3ref_qk_tokens_ex(P, qkv_rows, in_dt, w_q, w_k, tokens, n_tok, fp8, ds, 0, q, q_dt, k, k_dt,
+                              v, yf32, 0);
 }
 
 /* ------------------------------------------------------------------ decoder-block elementwise ops

@@ -175,3 +175,40 @@ def qk_amax(spec, qkv_bits, in_dt, w_q, w_k):
             m = np.abs(y[:, s])
             am[s] = np.nan if (np.isnan(m).any() or np.isnan(am[s])) else max(am[s], m.max())
     return am
+
+
+def qk_cast_static(spec, qkv_bits, in_dt, w_q, w_k, descale, v_fp8=False):
+    """FP8 cast with caller descales: (q, k, v, sat).  A descale that is not > 0 counts as 1; V is
+    cast with descale[2] when v_fp8, else copied; sat [3] counts |quotient| > 448 per tensor."""
+    B, T, H, D = spec.B, spec.T, spec.H, spec.D
+    flat = np.asarray(qkv_bits, np.uint16).reshape(-1)
+    d = np.ones(3, F)
+    given = np.asarray(descale, F).ravel()
+    d[:given.size] = given
+    ds = np.where(d > 0, d, F(1.0)).astype(F)
+    if not v_fp8:
+        ds[2] = F(1.0)
+    q = np.zeros((B, H, T, D), np.uint8)
+    k = np.zeros((B, H, T, D), np.uint8)
+    v = np.zeros((B, H, T, D), np.uint8 if v_fp8 else np.uint16)
+    sat = np.zeros(3, np.uint64)
+    for b in range(B):
+        vl = int(spec.vl[b])
+        if vl == 0:
+            continue
+        i = np.arange(vl)
+        start = b * spec.batch_stride + i[:, None] * spec.row_stride
+        rows_bits = flat[start + np.arange(3 * H * D)[None, :]]
+        y = token_y(spec, rows_bits, b * T + i, in_dt, w_q, w_k)   # [vl, 2, H, D]
+        vb = rows_bits[:, 2 * H * D:].reshape(vl, H, D)
+        parts = [(0, y[:, 0], q), (1, y[:, 1], k)]
+        if v_fp8:
+            parts.append((2, decode_in(vb, in_dt), v))
+        else:
+            v[b, :, :vl] = vb.transpose(1, 0, 2)
+        for s, val, out in parts:
+            with np.errstate(over="ignore", invalid="ignore"):
+                quo = (val / ds[s]).astype(F)
+                sat[s] += np.uint64(np.count_nonzero(np.abs(quo) > F(448.0)))
+            out[b, :, :vl] = e4m3_encode(quo).transpose(1, 0, 2)
+    return q, k, v, sat
