@@ -58,6 +58,8 @@ extern "C" {
 
 #define H3_ABI_VERSION 1
 #define H3_MAX_BATCH 64
+#define H3_SAT_SLOTS 128                       /* partial-count slots of a clip-counter buffer */
+#define H3_SAT_WORDS (16 * (H3_SAT_SLOTS + 1)) /* uint64 words of a clip-counter buffer */
 
 typedef enum { H3_F32 = 0, H3_F16 = 1, H3_BF16 = 2, H3_E4M3FN = 3 } h3_dtype;
 
@@ -128,12 +130,35 @@ int h3_qk_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
  *                      0xFF, sign not specified); 0x00 for padding tokens
  *   v_out              DEVICE [B, H, T, D], dtype in_dt: bit copy of the V heads (+0 for padding)
  *   descale_qk         DEVICE fp32 [2] out: the two descales for the attention consumer
- *   amax_qk            DEVICE fp32 [2] in (from h3_qk_amax, or 448 * a static descale)
+ *   amax_qk            DEVICE fp32 [2] in, from h3_qk_amax (static descales: see below)
  */
 int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
                     const float *w_q, const float *w_k, const float *amax_qk,
                     uint8_t *q_codes, uint8_t *k_codes, void *v_out, float *descale_qk,
                     hipStream_t stream);
+
+/*
+ * FP8 cast with static descales, no amax pass ([TRT-21485]: the static scale table offered as the
+ * alternative to dynamic scales, the per-tensor cast of Q, K and V, and the saturation log that
+ * counts elements clipped at the E4M3 range per tensor):
+ *   descale_qkv  DEVICE fp32 [2] (Q, K), or [3] (Q, K, V) when v_dt is H3_E4M3FN: the caller's
+ *                descales, read on the device; a value that is not > 0 (zero, negative, NaN) is
+ *                read as 1.  Any calibration margin is the caller's to apply.
+ *   q_codes / k_codes  DEVICE uint8 [B, H, T, D]: E4M3FN(RN(y' / descale_s)) as in h3_qk_cast_e4m3
+ *   v_out        DEVICE [B, H, T, D]: v_dt == in_dt: a bit copy of the V heads; v_dt == H3_E4M3FN:
+ *                uint8 codes E4M3FN(RN(v / descale_qkv[2])) of the V input values.  Padding: 0.
+ *   sat_qkv      DEVICE uint64 [H3_SAT_WORDS], or NULL: a clip-counter buffer, overwritten.
+ *                sat_qkv[0..2] receive the number of valid elements of Q, K, V whose binary32
+ *                quotient exceeds 448 in magnitude (saturated codes; a NaN quotient is not counted;
+ *                sat_qkv[2] = 0 when V is copied).  The rest of the buffer holds per-slot partial
+ *                counts (it is cleared, added to, then summed, all on the stream).  8-byte aligned,
+ *                not overlapping any other argument.
+ * With descale_s = amax_s / 448 this writes the codes h3_qk_cast_e4m3 writes.
+ */
+int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                           const float *w_q, const float *w_k, const float *descale_qkv,
+                           uint8_t *q_codes, uint8_t *k_codes, void *v_out, h3_dtype v_dt,
+                           uint64_t *sat_qkv, hipStream_t stream);
 
 /*
  * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,

@@ -217,6 +217,44 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, con
     return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
 }
 
+int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                           const float *w_k, const float *descale_qkv, uint8_t *q_codes, uint8_t *k_codes,
+                           void *v_out, h3_dtype v_dt, uint64_t *sat_qkv, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!descale_qkv || !q_codes || !k_codes || !v_out)
+        return fail(H3_EINVAL, "descale_qkv, q_codes, k_codes and v_out must be non-NULL");
+    if (v_dt != in_dt && v_dt != H3_E4M3FN) return fail(H3_EUNSUPPORTED, "v_dt must be in_dt or H3_E4M3FN");
+    const bool v_fp8 = v_dt == H3_E4M3FN;
+    if (reinterpret_cast<uintptr_t>(descale_qkv) & 3u) return fail(H3_EALIGN, "descale_qkv must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(sat_qkv) & 7u) return fail(H3_EALIGN, "sat_qkv must be 8-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(descale_qkv);
+    inputs.push_back({a, a + (v_fp8 ? 12u : 8u), "descale_qkv"});
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    std::vector<Range> outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
+                               out_range(v_out, n, v_dt, "v_out")};
+    rc = check_outputs(inputs, outs);
+    if (rc) return rc;
+    if (sat_qkv) {
+        const uintptr_t sp = reinterpret_cast<uintptr_t>(sat_qkv);
+        const Range sr = {sp, sp + (uintptr_t)H3_SAT_WORDS * 8, "sat_qkv"};
+        for (const Range &r : inputs)
+            if (overlaps(sr, r)) return fail(H3_EALIAS, std::string("sat_qkv overlaps input ") + r.name);
+        for (const Range &r : outs)
+            if (overlaps(sr, r)) return fail(H3_EALIAS, std::string("sat_qkv overlaps output ") + r.name);
+    }
+    p.amax = const_cast<float *>(descale_qkv);
+    p.static_scale = 1;
+    p.v_fp8 = v_fp8 ? 1 : 0;
+    p.sat = reinterpret_cast<unsigned long long *>(sat_qkv);
+    p.q = q_codes;
+    p.k = k_codes;
+    p.v = v_out;
+    return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
 int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream) {
     if (!x || !y) return fail(H3_EINVAL, "x and y must be non-NULL");
     if (dt != H3_F16 && dt != H3_BF16) return fail(H3_EUNSUPPORTED, "dt must be H3_F16 or H3_BF16");

@@ -58,8 +58,10 @@ struct QkParams {
     const float *wk;
     const float *cos_tab;
     const float *sin_tab;
-    float *amax;        // MODE_AMAX: reduced into (cleared first); MODE_CAST: read
-    float *descale;     // MODE_CAST: written by the first wave
+    float *amax;        // MODE_AMAX: reduced into (cleared first); MODE_CAST: read (amaxes, or
+                        // descales when static_scale)
+    float *descale;     // MODE_CAST: written by the first wave, or null
+    unsigned long long *sat;  // MODE_CAST: per-tensor counts of |quotient| > 448 (cleared first), or null
     int64_t row_stride;
     int64_t batch_stride;
     int64_t items;               // B * groups * head_chunks
@@ -71,6 +73,8 @@ struct QkParams {
     DivMagic div_gw, div_gh;     // token -> (t, h, w) decode
     float eps;
     float inv_n;                 // 1 / n (pair -> axis decode), 0 when n = 0
+    int32_t static_scale;        // MODE_CAST: amax[] holds the caller's descales
+    int32_t v_fp8;               // MODE_CAST: V written as E4M3 codes with the third scale
     int32_t off[H3_MAX_BATCH][3];
     int32_t vlen[H3_MAX_BATCH];
 };

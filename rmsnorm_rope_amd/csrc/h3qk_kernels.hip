@@ -402,7 +402,7 @@ __device__ __forceinline__ void pack_e4m3(const float (&q)[W], bool hw, uint32_t
 
 // ------------------------------------------------------------------ store / cast kernel
 
-template <int D, int IN, int QT, int KT, int MODE, int NN>
+template <int D, int IN, int QT, int KT, int MODE, int NN, bool VF8>
 __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     constexpr int W = (D == 64) ? 4 : 8;
     constexpr int M = D / (8 * W);
@@ -410,25 +410,28 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     constexpr int HPW = kHeadsPerWave;
     static_assert(M >= 1 && 8 * W * M == D, "layout");
     static_assert(MODE == MODE_STORE || MODE == MODE_CAST, "store / cast kernel");
+    static_assert(!VF8 || MODE == MODE_CAST, "V codes only in the cast pass");
+    constexpr int NS = VF8 ? 3 : 2;  // scaled tensors: Q, K (and V)
 
     const int lane = threadIdx.x & 63;
     const int c = chunk_of_lane(lane & 7);  // chunk of the row this lane holds
     const int g = lane >> 3;
     const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    float ds[2] = {1.0f, 1.0f}, rcp[2] = {1.0f, 1.0f};
-    bool fast = false;
+    float ds[3] = {1.0f, 1.0f, 1.0f}, rcp[3] = {1.0f, 1.0f, 1.0f};
+    bool fast = true;
     if constexpr (MODE == MODE_CAST) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const float am = p.amax[s];
-            ds[s] = am > 0.0f ? am / 448.0f : 1.0f;
+        for (int s = 0; s < NS; ++s) {
+            const float a = p.amax[s];
+            // dynamic: amax / 448 (1 when amax is not > 0); static: the descale itself, 1 when not > 0
+            ds[s] = a > 0.0f ? (p.static_scale ? a : a / 448.0f) : 1.0f;
             rcp[s] = 1.0f / ds[s];
+            fast = fast && ds[s] >= 0x1p-60f && ds[s] <= 0x1p60f;
         }
-        fast = ds[0] >= 0x1p-60f && ds[0] <= 0x1p60f && ds[1] >= 0x1p-60f && ds[1] <= 0x1p60f;
-        if (item == 0 && lane == 0) {
-            p.descale[0] = ds[0];
-            p.descale[1] = ds[1];
+        if (p.descale && item == 0 && lane == 0) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) p.descale[s] = ds[s];
         }
     }
     if (item >= p.items) return;
@@ -459,10 +462,19 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 store_zero_chunk<QT, W>(p.q, o + (olane + 8 * W * m + W * c));
                 store_zero_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c));
             }
+            if constexpr (VF8) {  // D bytes per token row: 8 or 16 bytes per lane
+                if constexpr (VC == 2)
+                    st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(p.v) + o + (olane + 16 * c)),
+                          (u32x4){0u, 0u, 0u, 0u});
+                else
+                    st_nt(reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(p.v) + o + (olane + 8 * c)),
+                          (u32x2){0u, 0u});
+            } else {
 #pragma unroll
-            for (int vc = 0; vc < VC; ++vc)
-                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)),
-                      (u32x4){0u, 0u, 0u, 0u});
+                for (int vc = 0; vc < VC; ++vc)
+                    st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)),
+                          (u32x4){0u, 0u, 0u, 0u});
+            }
         }
         return;
     }
@@ -532,6 +544,7 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
         row_scale_rotate<W, M>(xk, rr[2 * u + 1], wk, cs, sn, rot);
         if constexpr (MODE == MODE_CAST) {
             float qq[2][M][W];
+            float xv[VF8 ? VC : 1][8], qv[VF8 ? VC : 1][8];
             bool bad = false;  // a quotient above 448 in magnitude or NaN
 #pragma unroll
             for (int m = 0; m < M; ++m)
@@ -541,8 +554,36 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                     qq[1][m][k] = quotient(xk[m][k], ds[1], rcp[1]);
                     bad = bad || !(__builtin_fabsf(qq[0][m][k]) <= 448.0f) || !(__builtin_fabsf(qq[1][m][k]) <= 448.0f);
                 }
-            // rare (saturation, non-finite data, extreme descales): one branch for the whole wave
-            const bool exact = !fast || __builtin_amdgcn_ballot_w64(bad) != 0;
+            if constexpr (VF8) {
+#pragma unroll
+                for (int vc = 0; vc < VC; ++vc)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t wd = rv[u][vc][e >> 1];
+                        xv[vc][e] = in_to_f32<IN>((e & 1) ? (wd >> 16) : (wd & 0xFFFFu));
+                        qv[vc][e] = quotient(xv[vc][e], ds[2], rcp[2]);
+                        bad = bad || !(__builtin_fabsf(qv[vc][e]) <= 448.0f);
+                    }
+            }
+            // exact: NaN data or an extreme descale (rare): correctly rounded division where the
+            // quotient is out of the checked range, and the integer encoder, for the whole wave.
+            // clip: some quotient past the range (a descale below the data's amax / 448): it saturates.
+            bool exact = !fast, clip = false;
+            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                bool nan = false;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int k = 0; k < W; ++k) nan = nan || qq[0][m][k] != qq[0][m][k] || qq[1][m][k] != qq[1][m][k];
+                if constexpr (VF8) {
+#pragma unroll
+                    for (int vc = 0; vc < VC; ++vc)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) nan = nan || qv[vc][e] != qv[vc][e];
+                }
+                exact = exact || __builtin_amdgcn_ballot_w64(nan) != 0;
+                clip = true;
+            }
             if (exact) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
@@ -551,6 +592,52 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                         if (!fast || !(__builtin_fabsf(qq[0][m][k]) <= 448.0f)) qq[0][m][k] = xq[m][k] / ds[0];
                         if (!fast || !(__builtin_fabsf(qq[1][m][k]) <= 448.0f)) qq[1][m][k] = xk[m][k] / ds[1];
                     }
+                if constexpr (VF8) {
+#pragma unroll
+                    for (int vc = 0; vc < VC; ++vc)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (!fast || !(__builtin_fabsf(qv[vc][e]) <= 448.0f)) qv[vc][e] = xv[vc][e] / ds[2];
+                }
+            }
+            if (p.sat && (clip || exact)) {  // count quotients past the range over the active lanes
+                uint32_t n0 = 0, n1 = 0, n2 = 0;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int k = 0; k < W; ++k) {
+                        n0 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(qq[0][m][k]) > 448.0f));
+                        n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(qq[1][m][k]) > 448.0f));
+                    }
+                if constexpr (VF8) {
+#pragma unroll
+                    for (int vc = 0; vc < VC; ++vc)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            n2 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(qv[vc][e]) > 448.0f));
+                }
+                if (lane == (int)__builtin_ctzll(__builtin_amdgcn_read_exec())) {
+                    // partial counts spread over slots (one 128-byte line each) to keep atomics apart
+                    unsigned long long *slot = p.sat + 16 * (1 + (blockIdx.x & (H3_SAT_SLOTS - 1)));
+                    if (n0) atomicAdd(slot, (unsigned long long)n0);
+                    if (n1) atomicAdd(slot + 1, (unsigned long long)n1);
+                    if (n2) atomicAdd(slot + 2, (unsigned long long)n2);
+                }
+            }
+            if (clip && !exact) {  // no NaN here: saturate to +-448 ahead of the conversion instruction
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int k = 0; k < W; ++k) {
+                        qq[0][m][k] = __builtin_amdgcn_fmed3f(qq[0][m][k], -448.0f, 448.0f);
+                        qq[1][m][k] = __builtin_amdgcn_fmed3f(qq[1][m][k], -448.0f, 448.0f);
+                    }
+                if constexpr (VF8) {
+#pragma unroll
+                    for (int vc = 0; vc < VC; ++vc)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) qv[vc][e] = __builtin_amdgcn_fmed3f(qv[vc][e], -448.0f, 448.0f);
+                }
             }
             uint32_t cw[2][M][W / 4];
 #pragma unroll
@@ -568,6 +655,17 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                     store_code_words<W>(p.k, o + (olane + 8 * W * m + W * c), cw[1][m]);
                 }
             }
+            if constexpr (VF8) {
+                uint32_t cv[VC][2];
+#pragma unroll
+                for (int vc = 0; vc < VC; ++vc) pack_e4m3<8>(qv[vc], !exact, cv[vc]);
+                if constexpr (VC == 2) {  // each token's 128-byte row in one instruction
+                    store_words_pairs<1, 8>(p.v, o + olane, c, cv[0], cv[1]);
+                } else {  // 8 tokens' 64-byte rows: 512 contiguous bytes
+                    st_nt(reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(p.v) + o + (olane + 8 * c)),
+                          (u32x2){cv[0][0], cv[0][1]});
+                }
+            }
         } else {
             if constexpr (kPairStore<QT, W, M>) {
                 store_row_pairs<QT, W>(p.q, o + olane, c, xq);
@@ -582,9 +680,11 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c), xk[m]);
             }
         }
+        if constexpr (!VF8) {
 #pragma unroll
-        for (int vc = 0; vc < VC; ++vc)
-            st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)), rv[u][vc]);
+            for (int vc = 0; vc < VC; ++vc)
+                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)), rv[u][vc]);
+        }
     }
 }
 
@@ -699,8 +799,32 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
     }
 }
 
-__global__ void clear2_kernel(float *a) {
-    if (threadIdx.x < 2) a[threadIdx.x] = 0.0f;
+// Zero n words (the amax pair before its reduction, the clip counters before the cast).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *a, int n) {
+    for (int i = (int)threadIdx.x; i < n; i += 256) a[i] = 0u;
+}
+
+int clear_words(uint32_t *a, int n, hipStream_t stream, const char *what, std::string *err) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, a, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        *err = std::string(what) + " clear launch failed: " + hipGetErrorString(e);
+        return H3_ELAUNCH;
+    }
+    return H3_OK;
+}
+
+// Totals of the clip-counter slots: sat[t] = sum over slots of sat[16 (1 + slot) + t], one wave.
+__global__ __launch_bounds__(64) void sat_total_kernel(unsigned long long *sat) {
+    const int l = threadIdx.x;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        unsigned long long v = 0;
+        for (int s = l; s < H3_SAT_SLOTS; s += 64) v += sat[16 * (1 + s) + t];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        if (l == 0) sat[t] = v;
+    }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -750,7 +874,7 @@ int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hip
 // slower).  The cap is imposed by reserving a third of the CU's LDS per block (the kernels use none).
 constexpr int kStoreBlocksPerCU = 3;
 
-template <int D, int IN, int QT, int KT, int MODE, int NN>
+template <int D, int IN, int QT, int KT, int MODE, int NN, bool VF8>
 int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
     DeviceFacts f;
     if (!device_facts(&f, err)) return H3_ELAUNCH;
@@ -763,21 +887,29 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
             *err = "occupancy query failed";
             return H3_ELAUNCH;
         }
-        hipLaunchKernelGGL(clear2_kernel, dim3(1), dim3(64), 0, stream, p.amax);
-        const hipError_t e0 = hipGetLastError();
-        if (e0 != hipSuccess) {
-            *err = std::string("amax clear launch failed: ") + hipGetErrorString(e0);
-            return H3_ELAUNCH;
-        }
+        const int rc = clear_words(reinterpret_cast<uint32_t *>(p.amax), 2, stream, "amax", err);
+        if (rc != H3_OK) return rc;
         // persistent waves, two rounds of resident blocks: one atomic per block and tensor
         int64_t blocks = (p.items + 3) / 4;
         const int64_t cap = 2 * (int64_t)max_blocks * f.cus;
         if (blocks > cap) blocks = cap;
         return launch_kernel(reinterpret_cast<const void *>(kern), blocks, 0, p, stream, err);
     } else {
-        auto kern = qk_kernel<D, IN, QT, KT, MODE, NN>;
+        auto kern = qk_kernel<D, IN, QT, KT, MODE, NN, VF8>;
+        if (MODE == MODE_CAST && p.sat) {
+            const int rc = clear_words(reinterpret_cast<uint32_t *>(p.sat), 2 * H3_SAT_WORDS, stream, "clip counter", err);
+            if (rc != H3_OK) return rc;
+        }
         const size_t lds = (size_t)(f.lds_per_cu / kStoreBlocksPerCU);
-        return launch_kernel(reinterpret_cast<const void *>(kern), (p.items + 3) / 4, lds, p, stream, err);
+        const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + 3) / 4, lds, p, stream, err);
+        if (rc != H3_OK || MODE != MODE_CAST || !p.sat) return rc;
+        hipLaunchKernelGGL(sat_total_kernel, dim3(1), dim3(64), 0, stream, p.sat);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            *err = std::string("clip counter total launch failed: ") + hipGetErrorString(e);
+            return H3_ELAUNCH;
+        }
+        return H3_OK;
     }
 }
 
@@ -786,15 +918,21 @@ int dispatch_out(int q_dt, int k_dt, QkParams &p, hipStream_t s, std::string *er
     if constexpr (MODE == MODE_STORE) {
 #define H3_QK(QT, KT)                                                                        \
     if (q_dt == QT && k_dt == KT)                                                            \
-        return p.n == D / 8 ? launch_one<D, IN, QT, KT, MODE, D / 8>(p, s, err)               \
-                            : launch_one<D, IN, QT, KT, MODE, 0>(p, s, err);
+        return p.n == D / 8 ? launch_one<D, IN, QT, KT, MODE, D / 8, false>(p, s, err)        \
+                            : launch_one<D, IN, QT, KT, MODE, 0, false>(p, s, err);
         H3_QK(DT_F32, DT_F16) H3_QK(DT_F32, DT_BF16) H3_QK(DT_F32, DT_F32)
         H3_QK(DT_F16, DT_F16) H3_QK(DT_F16, DT_BF16) H3_QK(DT_F16, DT_F32)
         H3_QK(DT_BF16, DT_F16) H3_QK(DT_BF16, DT_BF16) H3_QK(DT_BF16, DT_F32)
 #undef H3_QK
+    } else if constexpr (MODE == MODE_AMAX) {
+        return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, false>(p, s, err)
+                            : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, false>(p, s, err);
     } else {
-        return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8>(p, s, err)
-                            : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0>(p, s, err);
+        if (p.v_fp8)
+            return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, true>(p, s, err)
+                                : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, true>(p, s, err);
+        return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, false>(p, s, err)
+                            : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, false>(p, s, err);
     }
     *err = "unsupported output dtype combination";
     return H3_EUNSUPPORTED;

@@ -79,6 +79,21 @@ class DeviceProblem:
         return q, k, v, ds
 
 
+    def run_cast_static(self, descale, v_fp8=False, count=True, outs=None, stream=None):
+        """Static-scale cast: descale is a device fp32 tensor ([2] or [3]).  Returns
+        (q, k, v, sat) with sat the device int64 clip-counter buffer [SAT_WORDS] whose first three
+        words are the counts (None when count is False)."""
+        import torch
+        import rmsnorm_rope_amd as h3
+        if outs is None:
+            outs = (self.out("e4m3"), self.out("e4m3"), self.out("e4m3" if v_fp8 else self.in_dt),
+                    torch.empty(h3.SAT_WORDS, dtype=torch.int64, device=self.device) if count else None)
+        q, k, v, sat = outs
+        h3.h3_qk_cast_e4m3_static(self.desc, self.qkv, self.in_dt, self.wq, self.wk, descale, q, k, v,
+                                  "e4m3" if v_fp8 else self.in_dt, sat, stream=stream)
+        return q, k, v, sat
+
+
 def oracle_spec(wl: synth.Workload):
     import oracle
     return oracle.spec_from_workload(wl, batch_stride=wl.T * wl.stride)
@@ -97,4 +112,6 @@ def algorithmic_bytes(wl: synth.Workload, mode: str, q_dt="f32", k_dt="f16") -> 
         return valid * 2 * hd * 2
     if mode == "cast":
         return valid * 3 * hd * 2 + tok_all * hd * (1 + 1 + 2)
+    if mode == "cast_v8":
+        return valid * 3 * hd * 2 + tok_all * hd * (1 + 1 + 1)
     raise ValueError(mode)

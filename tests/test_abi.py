@@ -37,6 +37,13 @@ def test_exports_every_declared_symbol():
         assert hasattr(h3.lib(), n)
 
 
+def test_header_constants_match_binding():
+    src = open(os.path.join(ROOT, "include", "h3qk.h")).read()
+    assert int(re.search(r"#define H3_SAT_SLOTS (\d+)", src).group(1)) == h3.SAT_SLOTS
+    assert int(re.search(r"#define H3_MAX_BATCH (\d+)", src).group(1)) == h3.MAX_BATCH
+    assert h3.SAT_WORDS == 16 * (h3.SAT_SLOTS + 1)
+
+
 def test_abi_version():
     assert h3.h3_abi_version() == 1
 
@@ -125,6 +132,36 @@ def test_amax_and_cast_validation():
                            BASE + 0x30000000, BASE + 0x40000000, BASE + 0x50000000, BASE + 0x61000004,
                            stream=0)
     assert e.value.name == "H3_EALIGN"
+
+
+def _static(d, descale=BASE + 0x60000000, q=BASE + 0x30000000, k=BASE + 0x40000000, v=BASE + 0x50000000,
+            v_dt=h3.E4M3FN, sat=BASE + 0x61000000):
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qk_cast_e4m3_static(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, descale, q, k, v, v_dt,
+                                  sat, stream=0)
+    return e.value.name, h3.h3_last_error()
+
+
+def test_static_cast_validation():
+    d = desc(D=128, pairs_per_axis=16)
+    assert _static(d, descale=0)[0] == "H3_EINVAL"
+    assert _static(d, v=0)[0] == "H3_EINVAL"
+    assert _static(d, v_dt=h3.F16)[0] == "H3_EUNSUPPORTED"          # neither in_dt (bf16) nor E4M3
+    assert _static(d, v_dt=h3.F32)[0] == "H3_EUNSUPPORTED"
+    assert _static(d, descale=BASE + 0x60000002)[0] == "H3_EALIGN"
+    assert _static(d, sat=BASE + 0x61000004)[0] == "H3_EALIGN"
+    name, msg = _static(d, sat=BASE + 0x60000000 - 8 * h3.SAT_WORDS + 8)  # counter tail on the descales
+    assert name == "H3_EALIAS" and "sat_qkv" in msg and "descale_qkv" in msg
+    name, msg = _static(d, sat=BASE + 0x50000000 + 32 * 2 * 128 - 8)  # counter on the V codes' tail
+    assert name == "H3_EALIAS" and "v_out" in msg
+    name, msg = _static(d, k=BASE + 0x30000000 + 32 * 2 * 128 - 16)  # K codes on Q codes
+    assert name == "H3_EALIAS" and "k_codes" in msg
+    # V copied (v_dt = in_dt): the V output is 2 bytes per element, so a K placed one code plane after
+    # V's start overlaps it, while with V codes it does not
+    name, msg = _static(d, v=BASE + 0x50000000, k=BASE + 0x50000000 + 32 * 2 * 128, v_dt=h3.BF16)
+    assert name == "H3_EALIAS" and "v_out" in msg
+    # with V as codes that layout passes the overlap checks; an unaligned counter then still fails
+    assert _static(d, v=BASE + 0x50000000, k=BASE + 0x50000000 + 32 * 2 * 128, sat=BASE + 0x61000001)[0] == "H3_EALIGN"
 
 
 def test_null_descriptor():
