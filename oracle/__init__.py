@@ -53,6 +53,12 @@ def lib():
         L.h3ref_qk_cast_e4m3_static.argtypes = [P, vp, ctypes.c_int, fp, fp, fp, ctypes.c_int, vp, vp, vp, vp]
         L.h3ref_qk_tokens_ex.argtypes = [P, vp, ctypes.c_int, fp, fp, vp, i64, ctypes.c_int, fp, ctypes.c_int,
                                          vp, ctypes.c_int, vp, ctypes.c_int, vp, fp, vp]
+        L.h3ref_qkv_amax.argtypes = [P, vp, ctypes.c_int, fp, fp, fp]
+        L.h3ref_qkv_cast_e4m3.argtypes = [P, vp, ctypes.c_int, fp, fp, fp, vp, vp, vp, fp]
+        L.h3ref_tensor_norm_rope.argtypes = [P, vp, ctypes.c_int, fp, vp, ctypes.c_int, ctypes.c_int]
+        L.h3ref_tensor_amax.argtypes = [P, vp, ctypes.c_int, fp, fp]
+        L.h3ref_tensor_cast_e4m3.argtypes = [P, vp, ctypes.c_int, fp, ctypes.c_float, ctypes.c_int, vp,
+                                             ctypes.c_int, fp, vp]
         L.h3ref_static_descale.argtypes = [ctypes.c_float]
         L.h3ref_static_descale.restype = ctypes.c_float
         L.h3ref_norm_rope_row.argtypes = [fp, ctypes.c_int, fp, ctypes.c_float, ctypes.c_int, vp, vp, fp]
@@ -200,6 +206,78 @@ def qk_cast_e4m3_static(spec: Spec, qkv: np.ndarray, in_dt: str, w_q, w_k, desca
     if rc:
         raise ValueError(f"oracle: position outside the tables (rc={rc})")
     return q, k, v, sat
+
+
+def qkv_amax(spec: Spec, qkv: np.ndarray, in_dt: str, w_q, w_k) -> np.ndarray:
+    """amax of Q and K (normalised, rotated) and of V (the input values) over the valid rows."""
+    qkv = np.ascontiguousarray(qkv, dtype=np.uint16)
+    wq, wk = _f32(w_q), _f32(w_k)
+    amax = np.zeros(3, np.float32)
+    rc = lib().h3ref_qkv_amax(ctypes.byref(spec.c()), _ptr(qkv), DT[in_dt], _ptr(wq), _ptr(wk), _ptr(amax))
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return amax
+
+
+def qkv_cast_e4m3(spec: Spec, qkv: np.ndarray, in_dt: str, w_q, w_k, amax):
+    """Dynamic cast of Q, K and V; returns (q, k, v codes, descale[3])."""
+    qkv = np.ascontiguousarray(qkv, dtype=np.uint16)
+    wq, wk, am = _f32(w_q), _f32(w_k), _f32(amax)
+    assert am.size == 3
+    shape = (spec.B, spec.H, spec.T, spec.D)
+    q = np.empty(shape, np.uint8); k = np.empty(shape, np.uint8); v = np.empty(shape, np.uint8)
+    ds = np.zeros(3, np.float32)
+    rc = lib().h3ref_qkv_cast_e4m3(ctypes.byref(spec.c()), _ptr(qkv), DT[in_dt], _ptr(wq), _ptr(wk), _ptr(am),
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(ds))
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return q, k, v, ds
+
+
+def _tensor_args(spec, x, w):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.size >= (spec.B - 1) * spec.batch_stride + (spec.T - 1) * spec.row_stride + spec.H * spec.D
+    wp = None if w is None else _f32(w)
+    return x, wp, (0 if wp is None else _ptr(wp))
+
+
+def _out_shape(spec, layout):
+    return (spec.B, spec.H, spec.T, spec.D) if layout == 0 else (spec.B, spec.T, spec.H, spec.D)
+
+
+def tensor_norm_rope(spec: Spec, x: np.ndarray, in_dt: str, w, out_dt: str, layout: int = 0) -> np.ndarray:
+    """One separately projected tensor (spec.H = its heads, spec.row_stride = its token stride):
+    norm + RoPE with weight w, or the identity when w is None; layout 0 [B,H,T,D], 1 [B,T,H,D]."""
+    x, wp, wptr = _tensor_args(spec, x, w)
+    out = np.empty(_out_shape(spec, layout), NP_DT[out_dt])
+    rc = lib().h3ref_tensor_norm_rope(ctypes.byref(spec.c()), _ptr(x), DT[in_dt], wptr, _ptr(out), DT[out_dt],
+                                      layout)
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return out
+
+
+def tensor_amax(spec: Spec, x: np.ndarray, in_dt: str, w) -> float:
+    x, wp, wptr = _tensor_args(spec, x, w)
+    a = np.zeros(1, np.float32)
+    rc = lib().h3ref_tensor_amax(ctypes.byref(spec.c()), _ptr(x), DT[in_dt], wptr, _ptr(a))
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return a[0]
+
+
+def tensor_cast_e4m3(spec: Spec, x: np.ndarray, in_dt: str, w, scale: float, is_descale: bool, layout: int = 0):
+    """Codes E4M3(y' / ds): ds from an amax (is_descale False) or a caller descale (True).
+    Returns (codes, descale, clip count)."""
+    x, wp, wptr = _tensor_args(spec, x, w)
+    out = np.empty(_out_shape(spec, layout), np.uint8)
+    ds = np.zeros(1, np.float32)
+    sat = np.zeros(1, np.uint64)
+    rc = lib().h3ref_tensor_cast_e4m3(ctypes.byref(spec.c()), _ptr(x), DT[in_dt], wptr, ctypes.c_float(scale),
+                                      int(is_descale), _ptr(out), layout, _ptr(ds), _ptr(sat))
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return out, ds[0], int(sat[0])
 
 
 def static_descale(d: float) -> float:

@@ -408,6 +408,144 @@ int h3ref_qk_tokens(const h3ref_problem *P, const void *qkv_rows, int in_dt, con
                               v, yf32, 0);
 }
 
+/* ------------------------------------------------------------------ V in the FP8 recipe
+ * TensorRT-LLM PR #21485, the commits on the per-tensor FP8 recipe: Q, K and V are cast to E4M3,
+ * each with its own per-tensor scale.  V is not normalised: its amax is max |v| over the valid
+ * rows of the V heads, and its codes are E4M3(v / descale_v).
+ */
+
+/* amax[0], amax[1] as h3ref_qk_amax; amax[2] = max |v| over the valid V rows (NaN propagates). */
+int h3ref_qkv_amax(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q,
+                   const float *w_k, float amax[3]) {
+    int rc = h3ref_qk_amax(P, qkv, in_dt, w_q, w_k, amax);
+    if (rc) return rc;
+    int H = P->H, D = P->D;
+    amax[2] = 0.0f;
+    for (int b = 0; b < P->B; ++b)
+        for (int64_t i = 0; i < P->valid_len[b]; ++i) {
+            const uint16_t *row = (const uint16_t *)qkv + (int64_t)b * P->batch_stride + i * P->row_stride;
+            for (int64_t e = 0; e < (int64_t)H * D; ++e) {
+                float m = fabsf(load_in(row, in_dt, 2 * (int64_t)H * D + e));
+                if (isnan(m) || isnan(amax[2])) amax[2] = NAN;
+                else if (m > amax[2]) amax[2] = m;
+            }
+        }
+    return 0;
+}
+
+/* Dynamic cast of Q, K and V: descale_s = amax_s / 448 (1 when amax_s is not > 0); Q, K, V codes
+   head-major [B, H, T, D]; descale[3] receives the three descales. */
+int h3ref_qkv_cast_e4m3(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q,
+                        const float *w_k, const float amax[3], uint8_t *q, uint8_t *k, uint8_t *v,
+                        float descale[3]) {
+    store_opts so = {1, 1, {h3ref_descale(amax[0]), h3ref_descale(amax[1]), h3ref_descale(amax[2])}, 0};
+    if (descale) { descale[0] = so.ds[0]; descale[1] = so.ds[1]; descale[2] = so.ds[2]; }
+    return run_items(P, qkv, in_dt, w_q, w_k, &so, q, REF_E4M3, k, REF_E4M3, v);
+}
+
+/* ------------------------------------------------------------------ one separately projected tensor
+ * TensorRT-LLM PR #21485, the norm_rope_tensor commit: one [B, S, H, D] tensor of the asynchronous
+ * Ulysses path, which projects Q, K and V separately, goes through norm + RoPE (Q, K) or the
+ * identity (V) to a 16-bit dtype, or to FP8 codes with its per-tensor descale; and the split
+ * launch mode that runs the packed QKV through these per-tensor passes with the packed row stride.
+ * The problem's H is the tensor's head count; head h of token i of item b starts at element
+ * b * batch_stride + i * row_stride + h * D.  Output layout 0 is [B, H, T, D], layout 1 is
+ * [B, T, H, D].  Reading: with no weight (V) the value is the input itself, not normalised or
+ * rotated.
+ */
+
+static int64_t out_index(const h3ref_problem *P, int layout, int b, int h, int64_t i, int d) {
+    if (layout == 0) return (((int64_t)b * P->H + h) * P->T + i) * P->D + d;
+    return (((int64_t)b * P->T + i) * P->H + h) * P->D + d;
+}
+
+/* y' [H][D] of token i of item b.  Returns 1 for a padded token, 0, or -1 (position off the tables). */
+static int token_tensor(const h3ref_problem *P, const uint16_t *row, int in_dt, const float *w, int b,
+                        int64_t i, float *y) {
+    if (i >= P->valid_len[b]) return 1;
+    int H = P->H, D = P->D;
+    if (!w) {
+        for (int64_t e = 0; e < (int64_t)H * D; ++e) y[e] = load_in(row, in_dt, e);
+        return 0;
+    }
+    int rows[3];
+    if (h3ref_token_rows(P, b, i, rows) != 0) return -1;
+    const float *crow[3], *srow[3];
+    for (int a = 0; a < 3; ++a) {
+        crow[a] = P->cos_tab + (int64_t)rows[a] * P->n;
+        srow[a] = P->sin_tab + (int64_t)rows[a] * P->n;
+    }
+    float x[256];
+    for (int h = 0; h < H; ++h) {
+        for (int d = 0; d < D; ++d) x[d] = load_in(row, in_dt, (int64_t)h * D + d);
+        h3ref_norm_rope_row(x, D, w, P->eps, P->n, crow, srow, y + (int64_t)h * D);
+    }
+    return 0;
+}
+
+/* 16-bit or f32 output: out = RN_out_dt(y'), +0 for padded tokens. */
+int h3ref_tensor_norm_rope(const h3ref_problem *P, const void *x, int in_dt, const float *w, void *out,
+                           int out_dt, int layout) {
+    static float y[64 * 256];
+    if (P->H > 64 || P->D > 256) return -2;
+    for (int b = 0; b < P->B; ++b)
+        for (int64_t i = 0; i < P->T; ++i) {
+            const uint16_t *row = (const uint16_t *)x + (int64_t)b * P->batch_stride + i * P->row_stride;
+            int rc = token_tensor(P, row, in_dt, w, b, i, y);
+            if (rc < 0) return rc;
+            for (int h = 0; h < P->H; ++h)
+                for (int d = 0; d < P->D; ++d) {
+                    int64_t o = out_index(P, layout, b, h, i, d);
+                    if (rc == 1) memset((char *)out + o * dt_size(out_dt), 0, (size_t)dt_size(out_dt));
+                    else store_out(out, out_dt, o, y[(int64_t)h * P->D + d]);
+                }
+        }
+    return 0;
+}
+
+/* amax = max |y'| over the valid rows (NaN propagates; +0 when nothing is valid). */
+int h3ref_tensor_amax(const h3ref_problem *P, const void *x, int in_dt, const float *w, float *amax) {
+    static float y[64 * 256];
+    if (P->H > 64 || P->D > 256) return -2;
+    *amax = 0.0f;
+    for (int b = 0; b < P->B; ++b)
+        for (int64_t i = 0; i < P->valid_len[b]; ++i) {
+            const uint16_t *row = (const uint16_t *)x + (int64_t)b * P->batch_stride + i * P->row_stride;
+            int rc = token_tensor(P, row, in_dt, w, b, i, y);
+            if (rc < 0) return rc;
+            for (int64_t e = 0; e < (int64_t)P->H * P->D; ++e) {
+                float m = fabsf(y[e]);
+                if (isnan(m) || isnan(*amax)) *amax = NAN;
+                else if (m > *amax) *amax = m;
+            }
+        }
+    return 0;
+}
+
+/* FP8 codes E4M3(y' / ds) with ds = descale(scale) (is_descale == 0: scale is the amax) or
+   static_descale(scale) (is_descale == 1); *descale (optional) receives ds; *sat (optional) is
+   overwritten with the count of valid elements whose quotient exceeds 448 in magnitude. */
+int h3ref_tensor_cast_e4m3(const h3ref_problem *P, const void *x, int in_dt, const float *w, float scale,
+                           int is_descale, uint8_t *out, int layout, float *descale, uint64_t *sat) {
+    static float y[64 * 256];
+    if (P->H > 64 || P->D > 256) return -2;
+    float ds = is_descale ? h3ref_static_descale(scale) : h3ref_descale(scale);
+    if (descale) *descale = ds;
+    if (sat) *sat = 0;
+    for (int b = 0; b < P->B; ++b)
+        for (int64_t i = 0; i < P->T; ++i) {
+            const uint16_t *row = (const uint16_t *)x + (int64_t)b * P->batch_stride + i * P->row_stride;
+            int rc = token_tensor(P, row, in_dt, w, b, i, y);
+            if (rc < 0) return rc;
+            for (int h = 0; h < P->H; ++h)
+                for (int d = 0; d < P->D; ++d) {
+                    int64_t o = out_index(P, layout, b, h, i, d);
+                    out[o] = rc == 1 ? 0 : cast_one(y[(int64_t)h * P->D + d], ds, sat);
+                }
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ decoder-block elementwise ops
  * vllm-omni PR #6607, "Operations" table, SwiGLU and scaled-residual rows (and the B300 isolated
  * measurements in the review thread): SwiGLU is SiluAndMul applied to the FP16 output of w1 (gate =
