@@ -143,7 +143,19 @@ def bench_fp8(wl, steps, warmup):
     _, pk = time_launches(lambda: pb.run_cast_static(clip, v_fp8=True, outs=souts, stream=stream.cuda_stream),
                           steps, warmup, stream)
     bs = algorithmic_bytes(wl, "cast_v8")
-    return {"static_v8_us": round(ps * 1e3, 2), "static_v8_GBs": round(bs / ps / 1e6, 1),
+    # dynamic recipe with V cast: amax of Q, K and V in one pass, then the cast with V codes
+    am3 = torch.empty(3, dtype=torch.float32, device="cuda")
+    ds3 = torch.empty(3, dtype=torch.float32, device="cuda")
+    vo = pb.out("e4m3")
+    _, pa3 = time_launches(lambda: h3.h3_qkv_amax(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, stream=stream.cuda_stream),
+                           steps, warmup, stream)
+    _, pc3 = time_launches(lambda: h3.h3_qkv_cast_e4m3(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, souts[0], souts[1],
+                                                       vo, ds3, stream=stream.cuda_stream), steps, warmup, stream)
+    ba3 = algorithmic_bytes(wl, "amax_v")
+    return {"qkv_amax_us": round(pa3 * 1e3, 2), "qkv_amax_GBs": round(ba3 / pa3 / 1e6, 1),
+            "qkv_cast_us": round(pc3 * 1e3, 2), "qkv_cast_GBs": round(bs / pc3 / 1e6, 1),
+            "qkv_pair_frac_of_peak": round((ba3 + bs) / (pa3 + pc3) / 1e6 / HBM_PEAK_GBS, 4),
+            "static_v8_us": round(ps * 1e3, 2), "static_v8_GBs": round(bs / ps / 1e6, 1),
             "static_v8_frac_of_peak": round(bs / ps / 1e6 / HBM_PEAK_GBS, 4),
             "static_v8_clip2sd_us": round(pk * 1e3, 2), "static_v8_clip2sd_GBs": round(bs / pk / 1e6, 1),
             "amax_us": round(pa * 1e3, 2), "amax_GBs": round(ba / pa / 1e6, 1),
@@ -151,6 +163,32 @@ def bench_fp8(wl, steps, warmup):
             "pair_us": round((pa + pc) * 1e3, 2), "pair_GBs": round((ba + bc) / (pa + pc) / 1e6, 1),
             "pair_frac_of_peak": round((ba + bc) / (pa + pc) / 1e6 / HBM_PEAK_GBS, 4),
             "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1)}
+
+
+def bench_tensor(wl, steps, warmup):
+    """One separately projected tensor: the K heads of the workload copied out as a compact
+    [B, T, H, D] f16 tensor, normalised and rotated into f16 [B, T, H, D] (the layout of the
+    asynchronous Ulysses input); and V through the identity path (a plain streaming copy)."""
+    import torch
+
+    import rmsnorm_rope_amd as h3
+    from synth.problem import DeviceProblem
+    pb = DeviceProblem(wl, "cuda")
+    H, D, T = wl.H, wl.D, wl.T
+    kx = pb.qkv[:, :, H * D:2 * H * D].contiguous()
+    del pb.qkv
+    desc = h3.make_desc(wl.B, T, H, D, wl.grid, wl.n, wl.table_len, pb.cos, pb.sin, pos_offset=pb.off,
+                        valid_len=wl.valid_len, eps=wl.eps, row_stride=H * D, batch_stride=T * H * D)
+    out = torch.empty((wl.B, T, H, D), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    _, pk = time_launches(lambda: h3.h3_tensor_norm_rope(desc, kx, "f16", pb.wk, out, "f16", h3.LAYOUT_BTHD,
+                                                         stream=stream.cuda_stream), steps, warmup, stream)
+    _, pv = time_launches(lambda: h3.h3_tensor_norm_rope(desc, kx, "f16", None, out, "f16", h3.LAYOUT_BTHD,
+                                                         stream=stream.cuda_stream), steps, warmup, stream)
+    nb = int(wl.valid_len.sum()) * H * D * 2 + wl.B * T * H * D * 2
+    return {"shape": [wl.B, T, H, D], "k_norm_rope_us": round(pk * 1e3, 2), "k_GBs": round(nb / pk / 1e6, 1),
+            "k_frac_of_peak": round(nb / pk / 1e6 / HBM_PEAK_GBS, 4),
+            "identity_us": round(pv * 1e3, 2), "identity_GBs": round(nb / pv / 1e6, 1)}
 
 
 def bench_block_ops(steps, warmup, rotate=8):
@@ -324,6 +362,7 @@ def main():
                            "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
                            "buffer_sets_rotated": rot}
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
+        extra["tensor_latent_k"] = bench_tensor(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra.update(bench_block_ops(max(20, args.steps), args.warmup))
         out["extra"] = extra
     if not args.no_cpu_baseline:

@@ -63,6 +63,9 @@ extern "C" {
 
 typedef enum { H3_F32 = 0, H3_F16 = 1, H3_BF16 = 2, H3_E4M3FN = 3 } h3_dtype;
 
+/* Output layout of the one-tensor entry points. */
+typedef enum { H3_LAYOUT_BHTD = 0, H3_LAYOUT_BTHD = 1 } h3_layout;
+
 enum {
     H3_OK = 0,
     H3_EINVAL = -1,       /* null pointer, non-positive size, bad stride or eps */
@@ -73,7 +76,9 @@ enum {
     H3_ELAUNCH = -6       /* the HIP runtime refused the launch (message in h3_last_error) */
 };
 
-/* Problem description shared by the three QK entry points (a HOST struct). */
+/* Problem description shared by the QK entry points (a HOST struct).  The one-tensor entry points
+   read it for a single [B, T, H, D] tensor: H is that tensor's head count and row_stride, >= H*D,
+   the elements between its consecutive tokens. */
 typedef struct {
     int32_t B;                 /* items in the batch, 1..H3_MAX_BATCH */
     int32_t T;                 /* padded tokens per item (>= 1) */
@@ -159,6 +164,63 @@ int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_
                            const float *w_q, const float *w_k, const float *descale_qkv,
                            uint8_t *q_codes, uint8_t *k_codes, void *v_out, h3_dtype v_dt,
                            uint64_t *sat_qkv, hipStream_t stream);
+
+/*
+ * FP8 recipe with V cast too ([TRT-21485]: Q, K and V cast to E4M3 with per-tensor scales, a
+ * dynamic amax pass then a cast pass).  Amax pass over the fused projection:
+ *   amax_qkv  DEVICE fp32 [3], overwritten: [0], [1] as h3_qk_amax; [2] = max |v| over the valid
+ *             V rows (V is not normalised).  A NaN makes its entry NaN.
+ */
+int h3_qkv_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                const float *w_q, const float *w_k, float *amax_qkv, hipStream_t stream);
+
+/*
+ * Cast pass of the same recipe: descale_s = amax_qkv[s] / 448 if amax_qkv[s] > 0, else 1;
+ *   q_codes, k_codes  DEVICE uint8 [B, H, T, D]: as h3_qk_cast_e4m3
+ *   v_codes           DEVICE uint8 [B, H, T, D]: E4M3FN(RN(v / descale_2)); 0x00 for padding
+ *   descale_qkv       DEVICE fp32 [3] out
+ */
+int h3_qkv_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                     const float *w_q, const float *w_k, const float *amax_qkv,
+                     uint8_t *q_codes, uint8_t *k_codes, uint8_t *v_codes, float *descale_qkv,
+                     hipStream_t stream);
+
+/*
+ * One separately projected tensor ([TRT-21485] norm_rope_tensor commit: one [B, S, H, D] tensor
+ * of the asynchronous Ulysses path, norm + RoPE for Q or K, the identity for V, to a 16-bit dtype
+ * or to FP8 with its per-tensor descale; and the split mode that runs a packed QKV through the
+ * per-tensor passes with the packed row stride).
+ *   x    DEVICE in_dt: head h of token i of item b at x + b*batch_stride + i*row_stride + h*D
+ *        (a compact [B, T, H, D] tensor has row_stride = H*D; the K part of a fused projection is
+ *        x = qkv + H*D with row_stride = 3*H*D)
+ *   w    DEVICE fp32 [D]: the tensor's norm weight (y' as in the contract above), or NULL: the
+ *        identity (y' = x, neither normalised nor rotated)
+ *   out  DEVICE out_dt in {H3_F32, H3_F16, H3_BF16}: RN(y'), laid out [B, H, T, D]
+ *        (H3_LAYOUT_BHTD) or [B, T, H, D] (H3_LAYOUT_BTHD); padding tokens +0
+ */
+int h3_tensor_norm_rope(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w,
+                        void *out, h3_dtype out_dt, h3_layout out_layout, hipStream_t stream);
+
+/*
+ * Per-tensor amax of the same y': *amax = max |y'| over the valid rows (DEVICE fp32 [1],
+ * overwritten; NaN propagates; +0 when nothing is valid).
+ */
+int h3_tensor_amax(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w,
+                   float *amax, hipStream_t stream);
+
+/*
+ * Per-tensor E4M3 cast of the same y':
+ *   scale       DEVICE fp32 [1]: an amax (scale_is_descale = 0: descale = amax / 448 if > 0, else 1)
+ *               or a caller's descale (scale_is_descale = 1: used when > 0, else 1)
+ *   codes       DEVICE uint8, layout out_layout: E4M3FN(RN(y' / descale)), as h3_qk_cast_e4m3
+ *   descale     DEVICE fp32 [1] out, or NULL
+ *   sat         DEVICE uint64 [H3_SAT_WORDS], or NULL: a clip-counter buffer as in
+ *               h3_qk_cast_e4m3_static; sat[0] receives the count of valid elements whose quotient
+ *               exceeds 448 in magnitude (sat[1], sat[2] = 0)
+ */
+int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w,
+                        const float *scale, int scale_is_descale, uint8_t *codes,
+                        h3_layout out_layout, float *descale, uint64_t *sat, hipStream_t stream);
 
 /*
  * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,

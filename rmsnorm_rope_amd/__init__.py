@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 __all__ = [
     "F32", "F16", "BF16", "E4M3FN", "MAX_BATCH", "SAT_WORDS", "H3Error", "QkDesc", "make_desc", "lib",
     "h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_qk_cast_e4m3_static",
-    "h3_swiglu", "h3_scaled_residual",
+    "h3_qkv_amax", "h3_qkv_cast_e4m3", "h3_tensor_norm_rope", "h3_tensor_amax", "h3_tensor_cast_e4m3",
+    "LAYOUT_BHTD", "LAYOUT_BTHD", "h3_swiglu", "h3_scaled_residual",
     "h3_last_error", "h3_abi_version",
     "EXPORTS",
 ]
@@ -23,6 +24,7 @@ F32, F16, BF16, E4M3FN = 0, 1, 2, 3
 MAX_BATCH = 64
 SAT_SLOTS = 128
 SAT_WORDS = 16 * (SAT_SLOTS + 1)  # uint64 words of a clip-counter buffer (counts in words 0..2)
+LAYOUT_BHTD, LAYOUT_BTHD = 0, 1
 _DT = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3FN, "e4m3fn": E4M3FN}
 ERRORS = {0: "H3_OK", -1: "H3_EINVAL", -2: "H3_EUNSUPPORTED", -3: "H3_EALIGN", -4: "H3_ERANGE",
           -5: "H3_EALIAS", -6: "H3_ELAUNCH"}
@@ -31,6 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh3qk.so"
 
 # every function include/h3qk.h declares
 EXPORTS = ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_qk_cast_e4m3_static",
+           "h3_qkv_amax", "h3_qkv_cast_e4m3", "h3_tensor_norm_rope", "h3_tensor_amax", "h3_tensor_cast_e4m3",
            "h3_swiglu", "h3_scaled_residual", "h3_last_error", "h3_abi_version")
 
 
@@ -70,10 +73,14 @@ def lib():
         L.h3_qk_amax.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.h3_qk_cast_e4m3.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.h3_qk_cast_e4m3_static.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        L.h3_qkv_amax.argtypes = [D, vp, i32, vp, vp, vp, vp]
+        L.h3_qkv_cast_e4m3.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.h3_tensor_norm_rope.argtypes = [D, vp, i32, vp, vp, i32, i32, vp]
+        L.h3_tensor_amax.argtypes = [D, vp, i32, vp, vp, vp]
+        L.h3_tensor_cast_e4m3.argtypes = [D, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp]
         L.h3_swiglu.argtypes = [vp, i32, vp, ctypes.c_int64, ctypes.c_int64, vp]
         L.h3_scaled_residual.argtypes = [vp, vp, i32, vp, ctypes.c_int64, vp, ctypes.c_int64, ctypes.c_int64, vp]
-        for f in ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_qk_cast_e4m3_static",
-                  "h3_swiglu", "h3_scaled_residual"):
+        for f in EXPORTS[:-2]:
             getattr(L, f).restype = i32
         L.h3_last_error.restype = ctypes.c_char_p
         L.h3_last_error.argtypes = []
@@ -160,6 +167,38 @@ def h3_qk_cast_e4m3_static(desc: QkDesc, qkv, in_dt, w_q, w_k, descale_qkv, q_co
                                       _ptr(descale_qkv), _ptr(q_codes), _ptr(k_codes), _ptr(v_out), _dt(v_dt),
                                       _ptr(sat_qkv), _stream(stream))
     _check("h3_qk_cast_e4m3_static", rc)
+
+
+def h3_qkv_amax(desc: QkDesc, qkv, in_dt, w_q, w_k, amax_qkv, stream=None) -> None:
+    rc = lib().h3_qkv_amax(ctypes.byref(desc), _ptr(qkv), _dt(in_dt), _ptr(w_q), _ptr(w_k), _ptr(amax_qkv),
+                           _stream(stream))
+    _check("h3_qkv_amax", rc)
+
+
+def h3_qkv_cast_e4m3(desc: QkDesc, qkv, in_dt, w_q, w_k, amax_qkv, q_codes, k_codes, v_codes, descale_qkv,
+                     stream=None) -> None:
+    rc = lib().h3_qkv_cast_e4m3(ctypes.byref(desc), _ptr(qkv), _dt(in_dt), _ptr(w_q), _ptr(w_k), _ptr(amax_qkv),
+                                _ptr(q_codes), _ptr(k_codes), _ptr(v_codes), _ptr(descale_qkv), _stream(stream))
+    _check("h3_qkv_cast_e4m3", rc)
+
+
+def h3_tensor_norm_rope(desc: QkDesc, x, in_dt, w, out, out_dt, out_layout=LAYOUT_BHTD, stream=None) -> None:
+    rc = lib().h3_tensor_norm_rope(ctypes.byref(desc), _ptr(x), _dt(in_dt), _ptr(w), _ptr(out), _dt(out_dt),
+                                   int(out_layout), _stream(stream))
+    _check("h3_tensor_norm_rope", rc)
+
+
+def h3_tensor_amax(desc: QkDesc, x, in_dt, w, amax, stream=None) -> None:
+    rc = lib().h3_tensor_amax(ctypes.byref(desc), _ptr(x), _dt(in_dt), _ptr(w), _ptr(amax), _stream(stream))
+    _check("h3_tensor_amax", rc)
+
+
+def h3_tensor_cast_e4m3(desc: QkDesc, x, in_dt, w, scale, scale_is_descale: bool, codes, out_layout=LAYOUT_BHTD,
+                        descale=None, sat=None, stream=None) -> None:
+    rc = lib().h3_tensor_cast_e4m3(ctypes.byref(desc), _ptr(x), _dt(in_dt), _ptr(w), _ptr(scale),
+                                   int(bool(scale_is_descale)), _ptr(codes), int(out_layout), _ptr(descale),
+                                   _ptr(sat), _stream(stream))
+    _check("h3_tensor_cast_e4m3", rc)
 
 
 def h3_swiglu(x, dt, y, N: int, F: int, stream=None) -> None:

@@ -10,8 +10,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3qk.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("h3qk_kernels.hip", "h3_block_kernels.hip", "h3qk_api.cpp")]
-HEADERS = [os.path.join(ROOT, "include", "h3qk.h"), os.path.join(CSRC, "h3qk_internal.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("h3qk_kernels.hip", "h3_tensor_kernels.hip", "h3_block_kernels.hip",
+                                             "h3qk_api.cpp")]
+HEADERS = [os.path.join(ROOT, "include", "h3qk.h"), os.path.join(CSRC, "h3qk_internal.h"),
+           os.path.join(CSRC, "h3qk_device.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -30,12 +30,14 @@ int elem_size(int dt) { return dt == H3_F32 ? 4 : (dt == H3_E4M3FN ? 1 : 2); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Validate the descriptor and the input pointers shared by the three QK calls; fill the kernel
-// parameters.  Returns H3_OK or an error code with g_err set.
+// Validate the descriptor and the input pointers shared by the QK calls (tensors = 3: a fused
+// Q | K | V row) and the one-tensor calls (tensors = 1: w_q is the tensor's weight, NULL for the
+// identity; w_k unused); fill the kernel parameters.  Returns H3_OK or an error code with g_err set.
 int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q, const float *w_k,
-               h3::QkParams *p, std::vector<Range> *inputs) {
+               h3::QkParams *p, std::vector<Range> *inputs, int tensors = 3) {
     if (!d) return fail(H3_EINVAL, "desc is NULL");
-    if (!qkv || !w_q || !w_k) return fail(H3_EINVAL, "qkv, w_q and w_k must be non-NULL");
+    if (tensors == 3 && (!qkv || !w_q || !w_k)) return fail(H3_EINVAL, "qkv, w_q and w_k must be non-NULL");
+    if (tensors == 1 && !qkv) return fail(H3_EINVAL, "x must be non-NULL");
     if (d->pairs_per_axis > 0 && (!d->cos_tab || !d->sin_tab))
         return fail(H3_EINVAL, "cos_tab and sin_tab must be non-NULL when pairs_per_axis > 0");
     if (d->B < 1 || d->B > H3_MAX_BATCH) return fail(H3_EINVAL, "B must be in 1..H3_MAX_BATCH");
@@ -46,14 +48,15 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
     if (d->pairs_per_axis < 0 || 6 * (int64_t)d->pairs_per_axis > D)
         return fail(H3_EUNSUPPORTED, "pairs_per_axis n must satisfy 0 <= 6n <= D");
     if (!std::isfinite(d->eps) || d->eps < 0.0f) return fail(H3_EINVAL, "eps must be finite and >= 0");
-    if (d->row_stride < 3 * H * D) return fail(H3_EINVAL, "row_stride must be >= 3*H*D");
+    if (d->row_stride < tensors * H * D)
+        return fail(H3_EINVAL, tensors == 3 ? "row_stride must be >= 3*H*D" : "row_stride must be >= H*D");
     if (d->row_stride > ((int64_t)1 << 26)) return fail(H3_EINVAL, "row_stride must be <= 2^26 elements");
     if (B > 1 && d->batch_stride < T * d->row_stride) return fail(H3_EINVAL, "batch_stride must be >= T*row_stride");
     if (d->batch_stride < 0) return fail(H3_EINVAL, "batch_stride must be >= 0");
     if ((d->row_stride & 7) || (d->batch_stride & 7))
         return fail(H3_EALIGN, "row_stride and batch_stride must be multiples of 8 elements (16 bytes)");
-    if (!aligned16(qkv) || !aligned16(w_q) || !aligned16(w_k))
-        return fail(H3_EALIGN, "qkv, w_q and w_k must be 16-byte aligned");
+    if (!aligned16(qkv) || !aligned16(w_q) || (tensors == 3 && !aligned16(w_k)))
+        return fail(H3_EALIGN, tensors == 3 ? "qkv, w_q and w_k must be 16-byte aligned" : "x and w must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(d->cos_tab) & 3u) || (reinterpret_cast<uintptr_t>(d->sin_tab) & 3u))
         return fail(H3_EALIGN, "cos_tab and sin_tab must be 4-byte aligned");
     for (int a = 0; a < 3; ++a) {
@@ -77,10 +80,13 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
         return fail(H3_EINVAL, "problem too large");
 
     const uintptr_t q0 = reinterpret_cast<uintptr_t>(qkv);
-    const int64_t qkv_elems = (B - 1) * d->batch_stride + (T - 1) * d->row_stride + 3 * H * D;
-    inputs->push_back({q0, q0 + (uintptr_t)qkv_elems * 2, "qkv"});
-    inputs->push_back({reinterpret_cast<uintptr_t>(w_q), reinterpret_cast<uintptr_t>(w_q) + (uintptr_t)D * 4, "w_q"});
-    inputs->push_back({reinterpret_cast<uintptr_t>(w_k), reinterpret_cast<uintptr_t>(w_k) + (uintptr_t)D * 4, "w_k"});
+    const int64_t qkv_elems = (B - 1) * d->batch_stride + (T - 1) * d->row_stride + tensors * H * D;
+    inputs->push_back({q0, q0 + (uintptr_t)qkv_elems * 2, tensors == 3 ? "qkv" : "x"});
+    if (w_q)
+        inputs->push_back({reinterpret_cast<uintptr_t>(w_q), reinterpret_cast<uintptr_t>(w_q) + (uintptr_t)D * 4,
+                           tensors == 3 ? "w_q" : "w"});
+    if (tensors == 3)
+        inputs->push_back({reinterpret_cast<uintptr_t>(w_k), reinterpret_cast<uintptr_t>(w_k) + (uintptr_t)D * 4, "w_k"});
     const uintptr_t tab_bytes = (uintptr_t)(rows_total * d->pairs_per_axis) * 4;
     inputs->push_back({reinterpret_cast<uintptr_t>(d->cos_tab), reinterpret_cast<uintptr_t>(d->cos_tab) + tab_bytes, "cos_tab"});
     inputs->push_back({reinterpret_cast<uintptr_t>(d->sin_tab), reinterpret_cast<uintptr_t>(d->sin_tab) + tab_bytes, "sin_tab"});
@@ -106,9 +112,10 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
         for (int a = 0; a < 3; ++a) p->off[b][a] = d->pos_offset[b][a];
         p->vlen[b] = d->valid_len[b];
     }
-    // Work items: 8 consecutive tokens x kHeadsPerWave heads, one wave each.
+    // Work items: 8 consecutive tokens x kHeadsPerWave (fused) or kTensorHeads heads, one wave each.
+    const int hpw = tensors == 3 ? h3::kHeadsPerWave : h3::kTensorHeads;
     p->groups = (int32_t)((T + 7) / 8);
-    p->head_chunks = (int32_t)((H + h3::kHeadsPerWave - 1) / h3::kHeadsPerWave);
+    p->head_chunks = (int32_t)((H + hpw - 1) / hpw);
     p->items = B * p->groups * p->head_chunks;
     if (p->items > INT32_MAX) return fail(H3_EINVAL, "problem too large");
     p->div_gw = h3::div_magic((uint32_t)d->grid[2]);
@@ -253,6 +260,160 @@ int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_
     p.k = k_codes;
     p.v = v_out;
     return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
+int h3_qkv_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                const float *w_k, float *amax_qkv, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!amax_qkv) return fail(H3_EINVAL, "amax_qkv must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(amax_qkv) & 3u) return fail(H3_EALIGN, "amax_qkv must be 4-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(amax_qkv);
+    for (const Range &in : inputs)
+        if (overlaps({a, a + 12, "amax_qkv"}, in)) return fail(H3_EALIAS, std::string("amax_qkv overlaps input ") + in.name);
+    p.amax = amax_qkv;
+    p.v_fp8 = 1;
+    return run(h3::MODE_AMAX, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
+int h3_qkv_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                     const float *w_k, const float *amax_qkv, uint8_t *q_codes, uint8_t *k_codes,
+                     uint8_t *v_codes, float *descale_qkv, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!amax_qkv || !q_codes || !k_codes || !v_codes || !descale_qkv)
+        return fail(H3_EINVAL, "amax_qkv, q_codes, k_codes, v_codes and descale_qkv must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(amax_qkv) & 3u) || (reinterpret_cast<uintptr_t>(descale_qkv) & 3u))
+        return fail(H3_EALIGN, "amax_qkv and descale_qkv must be 4-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(amax_qkv);
+    inputs.push_back({a, a + 12, "amax_qkv"});
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    std::vector<Range> outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
+                               out_range(v_codes, n, H3_E4M3FN, "v_codes")};
+    rc = check_outputs(inputs, outs);
+    if (rc) return rc;
+    const uintptr_t ds = reinterpret_cast<uintptr_t>(descale_qkv);
+    const Range dr = {ds, ds + 12, "descale_qkv"};
+    for (const Range &r : inputs)
+        if (overlaps(dr, r)) return fail(H3_EALIAS, std::string("descale_qkv overlaps input ") + r.name);
+    for (const Range &r : outs)
+        if (overlaps(dr, r)) return fail(H3_EALIAS, std::string("descale_qkv overlaps output ") + r.name);
+    p.amax = const_cast<float *>(amax_qkv);
+    p.v_fp8 = 1;
+    p.q = q_codes;
+    p.k = k_codes;
+    p.v = v_codes;
+    p.descale = descale_qkv;
+    return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
+}
+
+namespace {
+
+// Output strides of one tensor: [B, H, T, D] or [B, T, H, D].
+int tensor_layout(const h3_qk_desc *d, int layout, h3::QkParams *p) {
+    if (layout == H3_LAYOUT_BHTD) {
+        p->out_hstride = (int64_t)d->T * d->D;
+        p->out_tstride = d->D;
+    } else if (layout == H3_LAYOUT_BTHD) {
+        p->out_hstride = d->D;
+        p->out_tstride = (int64_t)d->H * d->D;
+    } else {
+        return fail(H3_EUNSUPPORTED, "out_layout must be H3_LAYOUT_BHTD or H3_LAYOUT_BTHD");
+    }
+    return H3_OK;
+}
+
+int run_tensor(int mode, int D, int in_dt, int out_dt, bool norm, h3::QkParams &p, hipStream_t stream) {
+    std::string err;
+    const int rc = h3::launch_tensor(mode, D, in_dt, out_dt, norm, p, stream, &err);
+    if (rc != H3_OK) return fail(rc, err);
+    g_err.clear();
+    return H3_OK;
+}
+
+}  // namespace
+
+int h3_tensor_norm_rope(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w, void *out,
+                        h3_dtype out_dt, h3_layout out_layout, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, x, in_dt, w, nullptr, &p, &inputs, 1);
+    if (rc) return rc;
+    if (!out) return fail(H3_EINVAL, "out must be non-NULL");
+    if (out_dt != H3_F32 && out_dt != H3_F16 && out_dt != H3_BF16)
+        return fail(H3_EUNSUPPORTED, "out_dt must be H3_F32, H3_F16 or H3_BF16");
+    rc = tensor_layout(desc, out_layout, &p);
+    if (rc) return rc;
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    rc = check_outputs(inputs, {out_range(out, n, out_dt, "out")});
+    if (rc) return rc;
+    p.wq = w;
+    p.q = out;
+    return run_tensor(h3::MODE_STORE, desc->D, in_dt, out_dt, w != nullptr, p, stream);
+}
+
+int h3_tensor_amax(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w, float *amax,
+                   hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, x, in_dt, w, nullptr, &p, &inputs, 1);
+    if (rc) return rc;
+    if (!amax) return fail(H3_EINVAL, "amax must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(amax) & 3u) return fail(H3_EALIGN, "amax must be 4-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(amax);
+    for (const Range &in : inputs)
+        if (overlaps({a, a + 4, "amax"}, in)) return fail(H3_EALIAS, std::string("amax overlaps input ") + in.name);
+    p.wq = w;
+    p.amax = amax;
+    return run_tensor(h3::MODE_AMAX, desc->D, in_dt, H3_E4M3FN, w != nullptr, p, stream);
+}
+
+int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w,
+                        const float *scale, int scale_is_descale, uint8_t *codes, h3_layout out_layout,
+                        float *descale, uint64_t *sat, hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, x, in_dt, w, nullptr, &p, &inputs, 1);
+    if (rc) return rc;
+    if (!scale || !codes) return fail(H3_EINVAL, "scale and codes must be non-NULL");
+    if (scale_is_descale != 0 && scale_is_descale != 1) return fail(H3_EINVAL, "scale_is_descale must be 0 or 1");
+    if ((reinterpret_cast<uintptr_t>(scale) & 3u) || (reinterpret_cast<uintptr_t>(descale) & 3u))
+        return fail(H3_EALIGN, "scale and descale must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(sat) & 7u) return fail(H3_EALIGN, "sat must be 8-byte aligned");
+    rc = tensor_layout(desc, out_layout, &p);
+    if (rc) return rc;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(scale);
+    inputs.push_back({a, a + 4, "scale"});
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    std::vector<Range> outs = {out_range(codes, n, H3_E4M3FN, "codes")};
+    rc = check_outputs(inputs, outs);
+    if (rc) return rc;
+    if (descale) {
+        const uintptr_t d = reinterpret_cast<uintptr_t>(descale);
+        outs.push_back({d, d + 4, "descale"});
+    }
+    if (sat) {
+        const uintptr_t sp = reinterpret_cast<uintptr_t>(sat);
+        outs.push_back({sp, sp + (uintptr_t)H3_SAT_WORDS * 8, "sat"});
+    }
+    for (size_t i = 1; i < outs.size(); ++i) {
+        for (const Range &r : inputs)
+            if (overlaps(outs[i], r)) return fail(H3_EALIAS, std::string(outs[i].name) + " overlaps input " + r.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(H3_EALIAS, std::string(outs[i].name) + " overlaps output " + outs[j].name);
+    }
+    p.wq = w;
+    p.amax = const_cast<float *>(scale);
+    p.static_scale = scale_is_descale;
+    p.descale = descale;
+    p.sat = reinterpret_cast<unsigned long long *>(sat);
+    p.q = codes;
+    return run_tensor(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, w != nullptr, p, stream);
 }
 
 int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream) {

@@ -1,0 +1,388 @@
+// Device-side building blocks shared by the gfx950 kernels of libh3qk: element conversions,
+// DPP butterflies, chunk loads and nontemporal stores, the normalised and rotated row in the
+// lane layout described in h3qk_kernels.hip, rotary-table entries, the correctly rounded
+// quotient and the E4M3 packing.  Internal: included by the kernel sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "h3qk_internal.h"
+
+namespace h3 {
+namespace {
+
+constexpr int DT_F32 = H3_F32, DT_F16 = H3_F16, DT_BF16 = H3_BF16, DT_E4M3 = H3_E4M3FN;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ element conversions
+
+template <int IN>
+__device__ __forceinline__ float in_to_f32(uint32_t bits16) {
+    if constexpr (IN == DT_BF16) {
+        return __uint_as_float(bits16 << 16);
+    } else {
+        _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+        return (float)h;  // exact
+    }
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+    _Float16 h = (_Float16)x;  // v_cvt_f16_f32: round to nearest even, IEEE denormals
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    __bf16 h = (__bf16)x;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// binary32 -> OCP E4M3FN, round to nearest even, saturating to +-448 (also +-inf), NaN -> 0x7F
+// with the sign.  Integer arithmetic on the encoding.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t E = a >> 23;
+    uint32_t sig = (a & 0x7FFFFFu) | (E ? 0x800000u : 0u);
+    bool normal = E >= 121u;                       // |f| >= 2^-6
+    uint32_t s = normal ? 20u : min(141u - E, 31u);
+    uint32_t base = normal ? (E - 121u) << 3 : 0u;
+    uint32_t q = sig >> s;
+    uint32_t rem = sig & ((1u << s) - 1u);
+    uint32_t half = 1u << (s - 1u);
+    q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+    uint32_t code = base + q;
+    code = a > 0x43E00000u ? 0x7Eu : code;         // > 448 saturates
+    code = a > 0x7F800000u ? 0x7Fu : code;         // NaN
+    return code | sign;
+}
+
+template <int OT>
+__device__ __forceinline__ uint32_t encode_out(float x) {
+    if constexpr (OT == DT_F16) return f32_to_f16_bits(x);
+    else if constexpr (OT == DT_BF16) return f32_to_bf16_bits(x);
+    else return f32_to_e4m3(x);
+}
+
+// ------------------------------------------------------------------ cross-lane butterflies
+
+// Every source lane of these patterns exists, so bound_ctrl never applies; setting it lets the
+// compiler fold the move into the consuming add (v_add_f32 with a DPP source).
+__device__ __forceinline__ float lane_xor1(float v) {  // DPP quad_perm [1,0,3,2]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_xor2(float v) {  // DPP quad_perm [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_mirror8(float v) {  // DPP row_half_mirror: lane l <-> 7 - l
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+}
+
+// Chunk held by lane l of a token's 8 lanes: l for l < 4, 11 - l for l >= 4.  Chunk ch + 4 then
+// sits in the half-mirror lane 7 - ch, so the first cross-lane tree level pairs mirror lanes and
+// the next two pair lanes l ^ 2 and l ^ 1 (lane l >= 4 stands for node 7 - l = l ^ 7, whose
+// partners l ^ 7 ^ 2 and l ^ 7 ^ 1 live in lanes l ^ 2 and l ^ 1).  All three are DPP moves.
+__device__ __forceinline__ int chunk_of_lane(int l) { return l < 4 ? l : 11 - l; }
+
+// ------------------------------------------------------------------ loads and stores
+
+// W consecutive 16-bit values (W = 4: 8 bytes, W = 8: 16 bytes) as W/2 packed words.
+template <int W>
+__device__ __forceinline__ void load_chunk(const uint16_t *p, uint32_t (&r)[W / 2]) {
+    if constexpr (W == 4) {
+        const u32x2 t = *reinterpret_cast<const u32x2 *>(p);
+        r[0] = t.x; r[1] = t.y;
+    } else {
+        const u32x4 t = *reinterpret_cast<const u32x4 *>(p);
+        r[0] = t.x; r[1] = t.y; r[2] = t.z; r[3] = t.w;
+    }
+}
+
+__device__ __forceinline__ void st_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(f32x4 *p, f32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// Store W encoded values of one chunk in output dtype OT at element offset `e` of `base`.
+template <int OT, int W>
+__device__ __forceinline__ void store_codes(void *base, int64_t e, const uint32_t (&w)[W]) {
+    if constexpr (OT == DT_E4M3) {
+        uint8_t *p = reinterpret_cast<uint8_t *>(base) + e;
+        uint32_t pk[W / 4];
+#pragma unroll
+        for (int k = 0; k < W; k += 4) pk[k / 4] = w[k] | (w[k + 1] << 8) | (w[k + 2] << 16) | (w[k + 3] << 24);
+        if constexpr (W == 4) st_nt(reinterpret_cast<uint32_t *>(p), pk[0]);
+        else st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){pk[0], pk[1]});
+    } else {
+        uint16_t *p = reinterpret_cast<uint16_t *>(base) + e;
+        uint32_t pk[W / 2];
+#pragma unroll
+        for (int k = 0; k < W; k += 2) pk[k / 2] = w[k] | (w[k + 1] << 16);
+        if constexpr (W == 4) st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){pk[0], pk[1]});
+        else st_nt(reinterpret_cast<u32x4 *>(p), (u32x4){pk[0], pk[1], pk[2], pk[3]});
+    }
+}
+
+template <int OT, int W>
+__device__ __forceinline__ void store_chunk(void *base, int64_t e, const float (&y)[W]) {
+    if constexpr (OT == DT_F32) {
+        float *p = reinterpret_cast<float *>(base) + e;
+#pragma unroll
+        for (int k = 0; k < W; k += 4)
+            st_nt(reinterpret_cast<f32x4 *>(p + k), (f32x4){y[k], y[k + 1], y[k + 2], y[k + 3]});
+    } else {
+        uint32_t w[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) w[k] = encode_out<OT>(y[k]);
+        store_codes<OT, W>(base, e, w);
+    }
+}
+
+template <int OT, int W>
+__device__ __forceinline__ void store_zero_chunk(void *base, int64_t e) {
+    if constexpr (OT == DT_F32) {
+        float *p = reinterpret_cast<float *>(base) + e;
+#pragma unroll
+        for (int k = 0; k < W; k += 4) st_nt(reinterpret_cast<f32x4 *>(p + k), (f32x4){0.f, 0.f, 0.f, 0.f});
+    } else {
+        uint32_t w[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) w[k] = 0u;
+        store_codes<OT, W>(base, e, w);
+    }
+}
+
+// Whole-row store of the lane's M = 2 chunks when a chunk is 8 bytes (16-bit outputs with W = 4,
+// E4M3 codes with W = 8), given as two packed words per chunk: neighbouring lanes (chunks 2j and
+// 2j + 1, always lanes l and l ^ 1 under chunk_of_lane) swap halves with one DPP move per word,
+// so the even-chunk lane holds the 16 bytes of chunks 2j, 2j + 1 of the first half-row and the odd
+// one those of the second half-row.  One 16-byte store per lane then writes the token's row as
+// whole 128-byte lines, which reach HBM without relying on the L2 to merge half-line writes.
+template <int EB, int W>
+__device__ __forceinline__ void store_words_pairs(void *base, int64_t row_e, int c, const uint32_t (&m0)[2],
+                                                  const uint32_t (&m1)[2]) {
+    static_assert(EB * W == 8, "8-byte chunks");
+    const bool odd = c & 1;
+    const uint32_t s0 = odd ? m0[0] : m1[0], s1 = odd ? m0[1] : m1[1];
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xF, 0xF, true);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xF, 0xF, true);
+    const u32x4 v = odd ? (u32x4){r0, r1, m1[0], m1[1]} : (u32x4){m0[0], m0[1], r0, r1};
+    // even chunk 2j: elements [2j W, 2j W + 2W); odd chunk 2j + 1: [8W + 2j W, 8W + 2j W + 2W)
+    const int64_t e = row_e + (odd ? 8 * W + (c - 1) * W : c * W);
+    st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(base) + e * EB), v);
+}
+
+template <int OT, int W>
+__device__ __forceinline__ void store_row_pairs(void *base, int64_t row_e, int c, const float (&y)[2][W]) {
+    static_assert((OT == DT_F16 || OT == DT_BF16) && W == 4, "16-bit outputs, 4-wide chunks");
+    uint32_t m0[2], m1[2];
+    m0[0] = encode_out<OT>(y[0][0]) | (encode_out<OT>(y[0][1]) << 16);
+    m0[1] = encode_out<OT>(y[0][2]) | (encode_out<OT>(y[0][3]) << 16);
+    m1[0] = encode_out<OT>(y[1][0]) | (encode_out<OT>(y[1][1]) << 16);
+    m1[1] = encode_out<OT>(y[1][2]) | (encode_out<OT>(y[1][3]) << 16);
+    store_words_pairs<2, W>(base, row_e, c, m0, m1);
+}
+
+// W E4M3 codes (W / 4 packed words) at element e.
+template <int W>
+__device__ __forceinline__ void store_code_words(void *base, int64_t e, const uint32_t (&w)[W / 4]) {
+    uint8_t *p = reinterpret_cast<uint8_t *>(base) + e;
+    if constexpr (W == 4) st_nt(reinterpret_cast<uint32_t *>(p), w[0]);
+    else st_nt(reinterpret_cast<u32x2 *>(p), (u32x2){w[0], w[1]});
+}
+
+template <int OT, int W, int M>
+constexpr bool kPairStore = M == 2 && (OT == DT_F16 || OT == DT_BF16) && W == 4;
+
+// ------------------------------------------------------------------ the row
+
+// One Q or K head row is held as x[m][k] (dim 8W m + W c + k, c the lane's chunk).  Binary32,
+// one rounding per operation, the halving reduction tree of the contract, no contraction (built
+// with -ffp-contract=off).
+
+// Sum of squares of the row over the halving tree; every lane of the token ends with it.
+template <int W, int M>
+__device__ __forceinline__ float row_sumsq(const float (&x)[M][W]) {
+    float a[M][W];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W; ++k) a[m][k] = x[m][k] * x[m][k];
+    // tree levels o = 8W M/2 .. 8W: chunk m folds chunk m + om, inside the lane
+#pragma unroll
+    for (int om = M / 2; om >= 1; om /= 2)
+#pragma unroll
+        for (int m = 0; m < om; ++m)
+#pragma unroll
+            for (int k = 0; k < W; ++k) a[m][k] = a[m][k] + a[m + om][k];
+    // levels 4W, 2W, W across the token's 8 lanes (see chunk_of_lane)
+#pragma unroll
+    for (int k = 0; k < W; ++k) a[0][k] = a[0][k] + lane_mirror8(a[0][k]);
+#pragma unroll
+    for (int k = 0; k < W; ++k) a[0][k] = a[0][k] + lane_xor2(a[0][k]);
+#pragma unroll
+    for (int k = 0; k < W; ++k) a[0][k] = a[0][k] + lane_xor1(a[0][k]);
+    // levels W/2 .. 1 inside the chunk
+#pragma unroll
+    for (int o = W / 2; o >= 1; o /= 2)
+#pragma unroll
+        for (int k = 0; k < o; ++k) a[0][k] = a[0][k] + a[0][k + o];
+    return a[0][0];
+}
+
+// r = 1 / sqrt(ss * (1/D) + eps): correctly rounded sqrt, then correctly rounded division.
+__device__ __forceinline__ float row_rstd(float ss, float inv_d, float eps) {
+    const float ms = ss * inv_d;
+    const float v = ms + eps;
+    const float sq = __builtin_sqrtf(v);
+    return 1.0f / sq;
+}
+
+// y = (x r) w, then the rotation of the lane's pairs.
+template <int W, int M>
+__device__ __forceinline__ void row_scale_rotate(float (&x)[M][W], float r, const float (&w)[M][W],
+                                                 const float (&cs)[M][W / 2], const float (&sn)[M][W / 2],
+                                                 const bool (&rot)[M][W / 2]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const float t = x[m][k] * r;
+            x[m][k] = t * w[m][k];
+        }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) {
+            const float e = x[m][2 * q], f = x[m][2 * q + 1];
+            const float c = cs[m][q], s = sn[m][q];
+            const float ec = e * c, fs = f * s, es = e * s, fc = f * c;
+            const float e2 = ec - fs, f2 = es + fc;
+            x[m][2 * q] = rot[m][q] ? e2 : e;
+            x[m][2 * q + 1] = rot[m][q] ? f2 : f;
+        }
+}
+
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {  // DPP quad_perm [J,J,J,J]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), J * 0x55, 0xF, 0xF, true));
+}
+
+// The 1/rms of up to 4 rows of a token with one square root and one division per lane: lane l of
+// each quad takes row l, and a DPP quad broadcast hands row j's value to every lane.  The 8 lanes
+// of a token are two quads, and both compute the same rows.
+template <int R>
+__device__ __forceinline__ void rows_rstd(const float (&ss)[R], int lane, float inv_d, float eps, float (&r)[R]) {
+    static_assert(R >= 1 && R <= 4, "one quad");
+    const int lr = lane & 3;
+    float mine = ss[0];
+#pragma unroll
+    for (int j = 1; j < R; ++j) mine = lr == j ? ss[j] : mine;
+    const float rm = row_rstd(mine, inv_d, eps);
+    r[0] = quad_bcast<0>(rm);
+    if constexpr (R > 1) r[1] = quad_bcast<1>(rm);
+    if constexpr (R > 2) r[2] = quad_bcast<2>(rm);
+    if constexpr (R > 3) r[3] = quad_bcast<3>(rm);
+}
+
+template <int W, int M, int IN>
+__device__ __forceinline__ void unpack_row(const uint32_t (&r)[M][W / 2], float (&x)[M][W]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) {
+            x[m][2 * k] = in_to_f32<IN>(r[m][k] & 0xFFFFu);
+            x[m][2 * k + 1] = in_to_f32<IN>(r[m][k] >> 16);
+        }
+}
+
+template <int W, int M>
+__device__ __forceinline__ void load_weights(const float *wsrc, int c, float (&w)[M][W]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W; k += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(wsrc + 8 * W * m + W * c + k);
+            w[m][k] = a.x; w[m][k + 1] = a.y; w[m][k + 2] = a.z; w[m][k + 3] = a.w;
+        }
+}
+
+// Rotary entries of this lane's pairs for token i of item b.  Pair index pr (the dims 2 pr,
+// 2 pr + 1) rotates when pr < 3n, on axis pr / n at frequency pr mod n.  NN is n when it is known
+// at compile time (the natural split n = D / 8), else 0 and n is read from the parameters; the
+// axis then comes from floor((pr + 1/2) / n) in binary32, exact because pr + 1/2 is never a
+// multiple of n and the rounding error is far below the 1/(2n) margin for pr < 128.  With NN
+// known, chunks whose pairs all rotate (or none does) need no per-lane test.
+template <int W, int M, int NN>
+__device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, int c,
+                                               float (&cs)[M][W / 2], float (&sn)[M][W / 2],
+                                               bool (&rot)[M][W / 2]) {
+    const int n = NN ? NN : p.n;
+    const uint32_t ui = (uint32_t)i;
+    const uint32_t j = div_apply(ui, p.div_gw);   // i / Gw
+    const uint32_t tq = div_apply(j, p.div_gh);   // i / (Gh Gw)
+    const int row_t = (int)tq + p.off[b][0];
+    const int row_h = p.base_h + (int)(j - tq * (uint32_t)p.Gh) + p.off[b][1];
+    const int row_w = p.base_w + (int)(ui - j * (uint32_t)p.Gw) + p.off[b][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int q = 0; q < W / 2; ++q) {
+            const int pr = 4 * W * m + (W / 2) * c + q;  // chunk m spans pairs [4W m, 4W m + 4W)
+            if (NN && 4 * W * m + 4 * W <= 3 * NN) rot[m][q] = true;
+            else if (NN && 4 * W * m >= 3 * NN) rot[m][q] = false;
+            else rot[m][q] = pr < 3 * n;
+            const int axis = NN ? pr / (NN ? NN : 1) : (int)(((float)pr + 0.5f) * p.inv_n);
+            const int jj = pr - axis * n;
+            const int row = axis == 0 ? row_t : (axis == 1 ? row_h : row_w);
+            const int idx = row * n + jj;
+            cs[m][q] = rot[m][q] ? p.cos_tab[idx] : 1.0f;
+            sn[m][q] = rot[m][q] ? p.sin_tab[idx] : 0.0f;
+        }
+}
+
+// RN(y / ds) without a division instruction, for a descale ds in [2^-60, 2^60] with
+// rcp = RN(1 / ds): q0 = RN(y rcp) is within 1.5 ulps of y / ds, one FMA remainder correction makes
+// it faithful, and a second one then gives the correctly rounded quotient (Markstein's theorem on
+// correcting a faithful quotient with a correctly rounded reciprocal; IBM J. Res. Dev. 34(1), 1990).
+// Checked against correctly rounded division for every binary32 y with y / ds in [2^-12, 512) and
+// 80 descales.  The quotient's sign is that of y (ds > 0), which also fixes y = -0.  Quotients
+// below 2^-11 may lose accuracy to underflow in the remainders, but every value under 2^-10
+// encodes to a zero code either way.  The result is a correctly rounded division, so the
+// no-contraction rule of the arithmetic chain is untouched.
+__device__ __forceinline__ float quotient(float y, float ds, float rcp) {
+    const float q0 = y * rcp;
+    const float r0 = __builtin_fmaf(-q0, ds, y);
+    const float q1 = __builtin_fmaf(r0, rcp, q0);
+    const float r1 = __builtin_fmaf(-q1, ds, y);
+    return __builtin_copysignf(__builtin_fmaf(r1, rcp, q1), y);
+}
+
+// Codes of W quotients as W/4 packed words.  hw: the conversion instruction, exact for |q| <= 448
+// (the caller guarantees that range); otherwise the integer encoder (saturation, NaN).
+template <int W>
+__device__ __forceinline__ void pack_e4m3(const float (&q)[W], bool hw, uint32_t (&w)[W / 4]) {
+#pragma unroll
+    for (int k = 0; k < W; k += 4) {
+        if (hw) {
+            int t = __builtin_amdgcn_cvt_pk_fp8_f32(q[k], q[k + 1], 0, false);
+            w[k / 4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[k + 2], q[k + 3], t, true);
+        } else {
+            w[k / 4] = f32_to_e4m3(q[k]) | (f32_to_e4m3(q[k + 1]) << 8) | (f32_to_e4m3(q[k + 2]) << 16) |
+                       (f32_to_e4m3(q[k + 3]) << 24);
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+}  // namespace
+}  // namespace h3

@@ -46,7 +46,14 @@ H3_HD inline uint32_t div_apply(uint32_t n, const DivMagic &g) {
 #ifndef H3QK_NO_HIP
 enum Mode : int { MODE_STORE = 0, MODE_AMAX = 1, MODE_CAST = 2 };
 
-constexpr int kHeadsPerWave = 2;  // heads of one 8-token group served by one wave
+constexpr int kHeadsPerWave = 2;  // heads of one 8-token group served by one wave (fused Q, K, V)
+constexpr int kTensorHeads = 4;   // the same for one separately projected tensor
+
+// Resident blocks per CU of the streaming store / cast kernels (a cap imposed through LDS): 3 for
+// the fused kernels, 4 for the one-tensor kernels, whose waves move fewer bytes each (measured on
+// the full latent's K heads: 3 blocks 234 us, 4 blocks 175 us, 6-8 blocks within 1 % of 4).
+constexpr int kStoreBlocksPerCU = 3;
+constexpr int kTensorBlocksPerCU = 4;
 
 // Everything a QK kernel reads, passed by value in the kernel arguments (< 1.5 KiB).
 struct QkParams {
@@ -74,14 +81,38 @@ struct QkParams {
     float eps;
     float inv_n;                 // 1 / n (pair -> axis decode), 0 when n = 0
     int32_t static_scale;        // MODE_CAST: amax[] holds the caller's descales
-    int32_t v_fp8;               // MODE_CAST: V written as E4M3 codes with the third scale
+    int32_t v_fp8;               // MODE_CAST: V written as E4M3 codes with the third scale;
+                                 // MODE_AMAX: V's amax reduced into amax[2]
+    int64_t out_hstride;         // one tensor: output elements between heads
+    int64_t out_tstride;         // one tensor: output elements between tokens
     int32_t off[H3_MAX_BATCH][3];
     int32_t vlen[H3_MAX_BATCH];
 };
 
+// Device facts read once per process (all devices of one process are gfx950 parts).
+struct DeviceFacts {
+    int cus = 0;
+    int lds_per_cu = 0;
+};
+bool device_facts(DeviceFacts *f, std::string *err);
+
+// One launch of `kern` with 256-thread blocks and the parameters by value.
+int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err);
+
+// Zero n words on the stream (one block).
+int clear_words(uint32_t *a, int n, hipStream_t stream, const char *what, std::string *err);
+
+// sat[0..2] = sums of the clip-counter slots (one wave, on the stream).
+int sat_total(unsigned long long *sat, hipStream_t stream, std::string *err);
+
 // Launch one QK pass.  Returns H3_OK or H3_ELAUNCH / H3_EUNSUPPORTED with *err filled.
 int launch_qk(int mode, int D, int in_dt, int q_dt, int k_dt, QkParams &p, hipStream_t stream,
               std::string *err);
+
+// Launch one pass over a single separately projected tensor (mode as above; norm: with weight
+// p.wq, else the identity).  The output pointer is p.q.
+int launch_tensor(int mode, int D, int in_dt, int out_dt, bool norm, QkParams &p, hipStream_t stream,
+                  std::string *err);
 
 // Decoder-block elementwise ops (arguments already validated).
 int launch_swiglu(int dt, const void *x, void *y, int64_t N, int64_t F, hipStream_t stream, std::string *err);

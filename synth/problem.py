@@ -110,6 +110,8 @@ def algorithmic_bytes(wl: synth.Workload, mode: str, q_dt="f32", k_dt="f16") -> 
         return valid * 3 * hd * 2 + tok_all * hd * (size[q_dt] + size[k_dt] + 2)
     if mode == "amax":
         return valid * 2 * hd * 2
+    if mode == "amax_v":
+        return valid * 3 * hd * 2
     if mode == "cast":
         return valid * 3 * hd * 2 + tok_all * hd * (1 + 1 + 2)
     if mode == "cast_v8":

@@ -164,6 +164,66 @@ def test_static_cast_validation():
     assert _static(d, v=BASE + 0x50000000, k=BASE + 0x50000000 + 32 * 2 * 128, sat=BASE + 0x61000001)[0] == "H3_EALIGN"
 
 
+def test_qkv_fp8_validation():
+    d = desc(D=128, pairs_per_axis=16)
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qkv_amax(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x20000000 + 508, stream=0)
+    assert e.value.name == "H3_EALIAS"                                     # amax_qkv tail on w_q
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qkv_amax(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x60000002, stream=0)
+    assert e.value.name == "H3_EALIGN"
+    n = 32 * 2 * 128
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qkv_cast_e4m3(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x60000000,
+                            BASE + 0x30000000, BASE + 0x40000000, BASE + 0x40000000 + n - 16, BASE + 0x61000000,
+                            stream=0)
+    assert e.value.name == "H3_EALIAS" and "v_codes" in h3.h3_last_error()
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_qkv_cast_e4m3(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, BASE + 0x60000000,
+                            BASE + 0x30000000, BASE + 0x40000000, BASE + 0x50000000, BASE + 0x60000008,
+                            stream=0)
+    assert e.value.name == "H3_EALIAS" and "descale_qkv" in h3.h3_last_error()  # on amax_qkv[2]
+
+
+def _tensor_store(d, x=BASE, w=BASE + 0x20000000, out=BASE + 0x30000000, out_dt=h3.F16, layout=0):
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_tensor_norm_rope(d, x, h3.BF16, w, out, out_dt, layout, stream=0)
+    return e.value.name, h3.h3_last_error()
+
+
+def test_tensor_validation():
+    d = desc(D=128, pairs_per_axis=16, row_stride=2 * 128)          # one tensor of H = 2 heads
+    assert _tensor_store(d, out_dt=h3.E4M3FN)[0] == "H3_EUNSUPPORTED"
+    assert _tensor_store(d, layout=2)[0] == "H3_EUNSUPPORTED"
+    assert _tensor_store(d, x=0)[0] == "H3_EINVAL"
+    assert _tensor_store(d, out=0)[0] == "H3_EINVAL"
+    assert _tensor_store(d, w=BASE + 0x20000004)[0] == "H3_EALIGN"
+    name, msg = _tensor_store(d, out=BASE + 4096)                    # out inside x
+    assert name == "H3_EALIAS" and "x" in msg
+    assert _tensor_store(desc(D=128, pairs_per_axis=16, row_stride=2 * 128 - 8))[0] == "H3_EINVAL"
+    # identity (w = NULL) passes weight checks; an aliasing output still fails
+    assert _tensor_store(d, w=0, out=BASE + 64)[0] == "H3_EALIAS"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_tensor_amax(d, BASE, h3.BF16, 0, BASE + 16, stream=0)
+    assert e.value.name == "H3_EALIAS"
+    with pytest.raises(h3.H3Error) as e:
+        h3.h3_tensor_amax(d, BASE, h3.BF16, 0, 0, stream=0)
+    assert e.value.name == "H3_EINVAL"
+
+    def cast(scale=BASE + 0x60000000, is_ds=1, codes=BASE + 0x30000000, descale=BASE + 0x61000000,
+             sat=BASE + 0x62000000):
+        with pytest.raises(h3.H3Error) as e:
+            h3.h3_tensor_cast_e4m3(d, BASE, h3.BF16, BASE + 0x20000000, scale, is_ds, codes, 0, descale, sat, stream=0)
+        return e.value.name, h3.h3_last_error()
+    assert cast(scale=0)[0] == "H3_EINVAL"
+    assert h3.lib().h3_tensor_cast_e4m3(ctypes.byref(d), BASE, h3.BF16, BASE + 0x20000000, BASE + 0x60000000, 2,
+                                        BASE + 0x30000000, 0, None, None, None) == -1
+    assert cast(descale=BASE + 0x60000000)[0] == "H3_EALIAS"       # descale on the scale input
+    name, msg = cast(sat=BASE + 0x30000000 + 32 * 2 * 128 - 8)      # counters on the codes' tail
+    assert name == "H3_EALIAS" and "sat" in msg
+    assert cast(sat=BASE + 0x62000004)[0] == "H3_EALIGN"
+
+
 def test_null_descriptor():
     rc = h3.lib().h3_qk_rmsnorm_rope_permute(None, BASE, 1, BASE, BASE, BASE, 0, BASE, 1, BASE, None)
     assert rc == -1 and "desc" in h3.h3_last_error()
