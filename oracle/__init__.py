@@ -59,6 +59,7 @@ def lib():
         L.h3ref_tensor_amax.argtypes = [P, vp, ctypes.c_int, fp, fp]
         L.h3ref_tensor_cast_e4m3.argtypes = [P, vp, ctypes.c_int, fp, ctypes.c_float, ctypes.c_int, vp,
                                              ctypes.c_int, fp, vp]
+        L.h3ref_qk_sage.argtypes = [P, vp, ctypes.c_int, fp, fp, ctypes.c_float, fp, fp, vp]
         L.h3ref_static_descale.argtypes = [ctypes.c_float]
         L.h3ref_static_descale.restype = ctypes.c_float
         L.h3ref_norm_rope_row.argtypes = [fp, ctypes.c_int, fp, ctypes.c_float, ctypes.c_int, vp, vp, fp]
@@ -278,6 +279,19 @@ def tensor_cast_e4m3(spec: Spec, x: np.ndarray, in_dt: str, w, scale: float, is_
     if rc:
         raise ValueError(f"oracle: position outside the tables (rc={rc})")
     return out, ds[0], int(sat[0])
+
+
+def qk_sage(spec: Spec, qkv: np.ndarray, in_dt: str, w_q, w_k, kv_scale: float):
+    """Sage emission: (Q f32, K * kv_scale f32, V * kv_scale f16 bits), head-major [B, H, T, D]."""
+    qkv = np.ascontiguousarray(qkv, dtype=np.uint16)
+    wq, wk = _f32(w_q), _f32(w_k)
+    shape = (spec.B, spec.H, spec.T, spec.D)
+    q = np.empty(shape, np.float32); k = np.empty(shape, np.float32); v = np.empty(shape, np.uint16)
+    rc = lib().h3ref_qk_sage(ctypes.byref(spec.c()), _ptr(qkv), DT[in_dt], _ptr(wq), _ptr(wk),
+                             ctypes.c_float(kv_scale), _ptr(q), _ptr(k), _ptr(v))
+    if rc:
+        raise ValueError(f"oracle: position outside the tables (rc={rc})")
+    return q, k, v
 
 
 def static_descale(d: float) -> float:

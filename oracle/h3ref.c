@@ -546,6 +546,38 @@ int h3ref_tensor_cast_e4m3(const h3ref_problem *P, const void *x, int in_dt, con
     return 0;
 }
 
+/* ------------------------------------------------------------------ sage emission
+ * stable-diffusion.cpp PR #19, the commit on the sage path: the fused RoPE/permute op writes the
+ * head-major tensors the sage attention reads, F32 Q, F32 K * kv_scale and F16 V * kv_scale, with
+ * the arithmetic and rounding points of the unfused chain (scale, then cast).  Reading: K' =
+ * RN32(y'_K * kv_scale); V' = RN16(RN32(v * kv_scale)) with v the input value as binary32; Q = y'_Q.
+ * Padded tokens are +0.
+ */
+int h3ref_qk_sage(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q, const float *w_k,
+                  float kv_scale, float *q, float *k, uint16_t *v) {
+    static float yqk[2 * 64 * 256];
+    int H = P->H, D = P->D;
+    if (H > 64 || D > 256) return -2;
+    int64_t plane = (int64_t)H * P->T * D;
+    for (int b = 0; b < P->B; ++b)
+        for (int64_t i = 0; i < P->T; ++i) {
+            const uint16_t *row = (const uint16_t *)qkv + (int64_t)b * P->batch_stride + i * P->row_stride;
+            int rc = token_qk(P, row, in_dt, w_q, w_k, b, i, yqk);
+            if (rc < 0) return rc;
+            for (int h = 0; h < H; ++h)
+                for (int d = 0; d < D; ++d) {
+                    int64_t o = b * plane + ((int64_t)h * P->T + i) * D + d;
+                    if (rc == 1) { q[o] = 0.0f; k[o] = 0.0f; v[o] = 0; continue; }
+                    q[o] = yqk[(int64_t)h * D + d];
+                    float ks = yqk[((int64_t)H + h) * D + d] * kv_scale;
+                    k[o] = ks;
+                    float vs = load_in(row, in_dt, ((int64_t)2 * H + h) * D + d) * kv_scale;
+                    v[o] = h3ref_f16_encode(vs);
+                }
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ decoder-block elementwise ops
  * vllm-omni PR #6607, "Operations" table, SwiGLU and scaled-residual rows (and the B300 isolated
  * measurements in the review thread): SwiGLU is SiluAndMul applied to the FP16 output of w1 (gate =
