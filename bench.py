@@ -165,6 +165,20 @@ def bench_fp8(wl, steps, warmup):
             "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1)}
 
 
+def bench_sage(wl, steps, warmup, kv_scale=0.125):
+    """Sage emission on the workload: F32 Q, F32 K * kv_scale, F16 V * kv_scale head-major."""
+    import torch
+
+    from synth.problem import DeviceProblem, algorithmic_bytes
+    pb = DeviceProblem(wl, "cuda")
+    outs = (pb.out("f32"), pb.out("f32"), pb.out("f16"))
+    stream = torch.cuda.current_stream()
+    _, pk = time_launches(lambda: pb.run_sage(kv_scale, outs=outs, stream=stream.cuda_stream), steps, warmup, stream)
+    nb = algorithmic_bytes(wl, "sage")
+    return {"kernel_us": round(pk * 1e3, 2), "GBs": round(nb / pk / 1e6, 1),
+            "frac_of_peak": round(nb / pk / 1e6 / HBM_PEAK_GBS, 4), "tokens_per_ms": round(wl.B * wl.T / pk, 1)}
+
+
 def bench_tensor(wl, steps, warmup):
     """One separately projected tensor: the K heads of the workload copied out as a compact
     [B, T, H, D] f16 tensor, normalised and rotated into f16 [B, T, H, D] (the layout of the
@@ -362,6 +376,7 @@ def main():
                            "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
                            "buffer_sets_rotated": rot}
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
+        extra["sage_latent"] = bench_sage(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra["tensor_latent_k"] = bench_tensor(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra.update(bench_block_ops(max(20, args.steps), args.warmup))
         out["extra"] = extra

@@ -118,6 +118,18 @@ int h3_qk_rmsnorm_rope_permute(const h3_qk_desc *desc, const void *qkv, h3_dtype
                                void *v_out, hipStream_t stream);
 
 /*
+ * Sage emission ([SDCPP-19] sage commit: the fused RoPE/permute op writes the head-major tensors
+ * the sage attention reads, with the rounding points of the unfused scale-then-cast chain):
+ *   q_out  DEVICE fp32 [B, H, T, D]: y'_Q
+ *   k_out  DEVICE fp32 [B, H, T, D]: RN32(y'_K * kv_scale)
+ *   v_out  DEVICE fp16 [B, H, T, D]: RN16(RN32(v * kv_scale)), v the V input value (f16 or bf16)
+ *   kv_scale  HOST fp32, finite.  Padding tokens are +0.
+ */
+int h3_qk_rmsnorm_rope_permute_sage(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                                    const float *w_q, const float *w_k, float kv_scale,
+                                    float *q_out, float *k_out, uint16_t *v_out, hipStream_t stream);
+
+/*
  * FP8 amax pass: amax_qk[0] = max |y'| over the valid Q rows of all items, amax_qk[1] the same
  * over the valid K rows ([TRT-21485] Summary and valid-length commit).
  *   amax_qk  DEVICE fp32 [2], overwritten (cleared on the stream, then reduced into).
@@ -226,10 +238,11 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
  * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,
  * SwiGLU row: SiluAndMul after the FP16 w1 output):
  *   x  DEVICE dt [N][2F] row-major: gate g = x[:, :F], up u = x[:, F:]
- *   y  DEVICE dt [N][F]:  y = RN_dt( (g / (1 + exp(-g))) * u ), evaluated in binary32
+ *   y  DEVICE dt [N][F]:  y = RN_dt( s * u ), s = g / (1 + exp(-g)) in binary32
  * dt is H3_F16 or H3_BF16; F a multiple of 8; N * F / 8 < 2^32; x, y 16-byte aligned, not
  * overlapping.  exp and the reciprocal are the hardware binary32 approximations (relative error
- * below 1e-6), so y may sit one ulp of dt from the exactly rounded value.
+ * below 1e-6); the f16 product s * u is rounded once to f16 (a mixed-precision FMA), the bf16 one
+ * through binary32.  y may sit one ulp of dt from the exactly rounded value.
  */
 int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream);
 

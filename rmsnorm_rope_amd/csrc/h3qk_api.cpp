@@ -177,6 +177,27 @@ int h3_qk_rmsnorm_rope_permute(const h3_qk_desc *desc, const void *qkv, h3_dtype
     return run(h3::MODE_STORE, desc->D, in_dt, q_dt, k_dt, p, stream);
 }
 
+int h3_qk_rmsnorm_rope_permute_sage(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                                    const float *w_k, float kv_scale, float *q_out, float *k_out, uint16_t *v_out,
+                                    hipStream_t stream) {
+    h3::QkParams p;
+    std::vector<Range> inputs;
+    int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
+    if (rc) return rc;
+    if (!q_out || !k_out || !v_out) return fail(H3_EINVAL, "q_out, k_out and v_out must be non-NULL");
+    if (!std::isfinite(kv_scale)) return fail(H3_EINVAL, "kv_scale must be finite");
+    const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
+    rc = check_outputs(inputs, {out_range(q_out, n, H3_F32, "q_out"), out_range(k_out, n, H3_F32, "k_out"),
+                                out_range(v_out, n, H3_F16, "v_out")});
+    if (rc) return rc;
+    p.q = q_out;
+    p.k = k_out;
+    p.v = v_out;
+    p.sage = 1;
+    p.kv_scale = kv_scale;
+    return run(h3::MODE_STORE, desc->D, in_dt, H3_F32, H3_F32, p, stream);
+}
+
 int h3_qk_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
                const float *w_k, float *amax_qk, hipStream_t stream) {
     h3::QkParams p;

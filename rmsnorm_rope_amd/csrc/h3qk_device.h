@@ -61,6 +61,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
     return code | sign;
 }
 
+// The value as a materialised binary32: without this the compiler may fold a binary32 product of a
+// 16-bit input and its conversion to binary16 into one mixed-precision FMA (v_fma_mixlo_f16), which
+// rounds once where the contract rounds twice.
+__device__ __forceinline__ float keep_f32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 template <int OT>
 __device__ __forceinline__ uint32_t encode_out(float x) {
     if constexpr (OT == DT_F16) return f32_to_f16_bits(x);

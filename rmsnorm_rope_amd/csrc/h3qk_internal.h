@@ -83,6 +83,8 @@ struct QkParams {
     int32_t static_scale;        // MODE_CAST: amax[] holds the caller's descales
     int32_t v_fp8;               // MODE_CAST: V written as E4M3 codes with the third scale;
                                  // MODE_AMAX: V's amax reduced into amax[2]
+    int32_t sage;                // MODE_STORE: sage emission (F32 Q, F32 K * kv_scale, F16 V * kv_scale)
+    float kv_scale;
     int64_t out_hstride;         // one tensor: output elements between heads
     int64_t out_tstride;         // one tensor: output elements between tokens
     int32_t off[H3_MAX_BATCH][3];

@@ -37,8 +37,11 @@ namespace {
 
 // ------------------------------------------------------------------ store / cast kernel
 
-template <int D, int IN, int QT, int KT, int MODE, int NN, bool VF8>
+// VM: what V becomes.  0: a bit copy; 1 (cast pass): E4M3 codes with the third descale;
+// 2 (store pass, sage emission): RN16(v * kv_scale), with K also multiplied by kv_scale.
+template <int D, int IN, int QT, int KT, int MODE, int NN, int VM>
 __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
+    constexpr bool VF8 = VM == 1;
     constexpr int W = (D == 64) ? 4 : 8;
     constexpr int M = D / (8 * W);
     constexpr int VC = D / 64;  // 16-byte V chunks per lane
@@ -46,6 +49,7 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     static_assert(M >= 1 && 8 * W * M == D, "layout");
     static_assert(MODE == MODE_STORE || MODE == MODE_CAST, "store / cast kernel");
     static_assert(!VF8 || MODE == MODE_CAST, "V codes only in the cast pass");
+    static_assert(VM != 2 || (MODE == MODE_STORE && KT == DT_F32), "sage: f32 K from the store pass");
     constexpr int NS = VF8 ? 3 : 2;  // scaled tensors: Q, K (and V)
 
     const int lane = threadIdx.x & 63;
@@ -302,6 +306,12 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 }
             }
         } else {
+            if constexpr (VM == 2) {  // sage: K * kv_scale, rounded once in binary32
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int k = 0; k < W; ++k) xk[m][k] = xk[m][k] * p.kv_scale;
+            }
             if constexpr (kPairStore<QT, W, M>) {
                 store_row_pairs<QT, W>(p.q, o + olane, c, xq);
             } else {
@@ -315,10 +325,24 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c), xk[m]);
             }
         }
-        if constexpr (!VF8) {
+        if constexpr (VM == 0) {
 #pragma unroll
             for (int vc = 0; vc < VC; ++vc)
                 st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)), rv[u][vc]);
+        } else if constexpr (VM == 2) {  // sage: RN16(RN32(v * kv_scale))
+#pragma unroll
+            for (int vc = 0; vc < VC; ++vc) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t wd = rv[u][vc][e];
+                    const float lo = keep_f32(in_to_f32<IN>(wd & 0xFFFFu) * p.kv_scale);
+                    const float hi = keep_f32(in_to_f32<IN>(wd >> 16) * p.kv_scale);
+                    wv[e] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+                }
+                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)),
+                      (u32x4){wv[0], wv[1], wv[2], wv[3]});
+            }
         }
     }
 }
@@ -534,8 +558,9 @@ namespace {
 // about 7 % slower).  The cap is imposed by reserving a third of the CU's LDS per block (the kernels
 // use none).
 
-template <int D, int IN, int QT, int KT, int MODE, int NN, bool VF8>
+template <int D, int IN, int QT, int KT, int MODE, int NN, int VM>
 int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
+    constexpr bool VF8 = VM == 1;
     DeviceFacts f;
     if (!device_facts(&f, err)) return H3_ELAUNCH;
     if constexpr (MODE == MODE_AMAX) {
@@ -555,7 +580,7 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
         if (blocks > cap) blocks = cap;
         return launch_kernel(reinterpret_cast<const void *>(kern), blocks, 0, p, stream, err);
     } else {
-        auto kern = qk_kernel<D, IN, QT, KT, MODE, NN, VF8>;
+        auto kern = qk_kernel<D, IN, QT, KT, MODE, NN, VM>;
         if (MODE == MODE_CAST && p.sat) {
             const int rc = clear_words(reinterpret_cast<uint32_t *>(p.sat), 2 * H3_SAT_WORDS, stream, "clip counter", err);
             if (rc != H3_OK) return rc;
@@ -570,20 +595,23 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
 template <int D, int IN, int MODE>
 int dispatch_out(int q_dt, int k_dt, QkParams &p, hipStream_t s, std::string *err) {
     if constexpr (MODE == MODE_STORE) {
+        if (p.sage)  // F32 Q, F32 K * kv_scale, F16 V * kv_scale
+            return p.n == D / 8 ? launch_one<D, IN, DT_F32, DT_F32, MODE, D / 8, 2>(p, s, err)
+                                : launch_one<D, IN, DT_F32, DT_F32, MODE, 0, 2>(p, s, err);
 #define H3_QK(QT, KT)                                                                        \
     if (q_dt == QT && k_dt == KT)                                                            \
-        return p.n == D / 8 ? launch_one<D, IN, QT, KT, MODE, D / 8, false>(p, s, err)        \
-                            : launch_one<D, IN, QT, KT, MODE, 0, false>(p, s, err);
+        return p.n == D / 8 ? launch_one<D, IN, QT, KT, MODE, D / 8, 0>(p, s, err)            \
+                            : launch_one<D, IN, QT, KT, MODE, 0, 0>(p, s, err);
         H3_QK(DT_F32, DT_F16) H3_QK(DT_F32, DT_BF16) H3_QK(DT_F32, DT_F32)
         H3_QK(DT_F16, DT_F16) H3_QK(DT_F16, DT_BF16) H3_QK(DT_F16, DT_F32)
         H3_QK(DT_BF16, DT_F16) H3_QK(DT_BF16, DT_BF16) H3_QK(DT_BF16, DT_F32)
 #undef H3_QK
     } else {
         if (p.v_fp8)
-            return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, true>(p, s, err)
-                                : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, true>(p, s, err);
-        return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, false>(p, s, err)
-                            : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, false>(p, s, err);
+            return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, 1>(p, s, err)
+                                : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, 1>(p, s, err);
+        return p.n == D / 8 ? launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, D / 8, 0>(p, s, err)
+                            : launch_one<D, IN, DT_E4M3, DT_E4M3, MODE, 0, 0>(p, s, err);
     }
     *err = "unsupported output dtype combination";
     return H3_EUNSUPPORTED;

@@ -60,6 +60,14 @@ class DeviceProblem:
                                       stream=stream)
         return q, k, v
 
+    def run_sage(self, kv_scale, outs=None, stream=None):
+        """Sage emission: (Q f32, K * kv_scale f32, V * kv_scale f16)."""
+        import rmsnorm_rope_amd as h3
+        q, k, v = outs if outs is not None else (self.out("f32"), self.out("f32"), self.out("f16"))
+        h3.h3_qk_rmsnorm_rope_permute_sage(self.desc, self.qkv, self.in_dt, self.wq, self.wk, kv_scale, q, k, v,
+                                           stream=stream)
+        return q, k, v
+
     def run_amax(self, amax=None, stream=None):
         import torch
         import rmsnorm_rope_amd as h3
@@ -108,6 +116,8 @@ def algorithmic_bytes(wl: synth.Workload, mode: str, q_dt="f32", k_dt="f16") -> 
     hd = wl.H * wl.D
     if mode == "store":
         return valid * 3 * hd * 2 + tok_all * hd * (size[q_dt] + size[k_dt] + 2)
+    if mode == "sage":
+        return valid * 3 * hd * 2 + tok_all * hd * (4 + 4 + 2)
     if mode == "amax":
         return valid * 2 * hd * 2
     if mode == "amax_v":

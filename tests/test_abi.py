@@ -164,6 +164,20 @@ def test_static_cast_validation():
     assert _static(d, v=BASE + 0x50000000, k=BASE + 0x50000000 + 32 * 2 * 128, sat=BASE + 0x61000001)[0] == "H3_EALIGN"
 
 
+def test_sage_validation():
+    d = desc()
+    def sage(scale=0.125, q=BASE + 0x30000000, k=BASE + 0x40000000, v=BASE + 0x50000000):
+        with pytest.raises(h3.H3Error) as e:
+            h3.h3_qk_rmsnorm_rope_permute_sage(d, BASE, h3.F16, BASE + 0x20000000, BASE + 0x21000000, scale, q, k, v,
+                                               stream=0)
+        return e.value.name, h3.h3_last_error()
+    assert sage(scale=float("nan"))[0] == "H3_EINVAL"
+    assert sage(scale=float("inf"))[0] == "H3_EINVAL"
+    assert sage(v=0)[0] == "H3_EINVAL"
+    name, msg = sage(k=BASE + 0x30000000 + 32 * 2 * 64 * 4 - 16)   # K f32 on Q f32's tail
+    assert name == "H3_EALIAS" and "k_out" in msg
+
+
 def test_qkv_fp8_validation():
     d = desc(D=128, pairs_per_axis=16)
     with pytest.raises(h3.H3Error) as e:
