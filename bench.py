@@ -21,13 +21,18 @@ sys.path.insert(0, ROOT)
 METRIC = "fused QK-norm+RoPE+permute GB/s and tokens/ms; % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_latent.txt")
-KERNEL_SRC = os.path.join(ROOT, "rmsnorm_rope_amd", "csrc", "h3qk_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "rmsnorm_rope_amd", "csrc", f) for f in ("h3qk_kernels.hip", "h3qk_device.h",
+                                                                       "h3qk_internal.h")]
 
 
 def kernel_digest() -> str:
+    """Digest of the sources the fused kernels are built from (kernel file and device helpers)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(bytes_alg):
@@ -49,25 +54,22 @@ def measured_traffic(bytes_alg):
 
 
 def time_launches(launch, steps, warmup, stream):
-    """Run `launch` warmup + steps times on `stream`; returns (total ms over the timed region,
-    mean per-launch ms from event pairs around each launch)."""
+    """Run `launch` warmup times untimed, then `steps` times back to back between two HIP events
+    recorded on `stream` (synchronised on both sides).  Returns (total ms of the timed region,
+    average ms per launch = total / steps).  No event sits between the timed launches, so the
+    average is the launch-to-launch time of a steady stream of calls."""
     import torch
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
-    for a, b in ev:
-        a.record(stream)
+    for _ in range(steps):
         launch()
-        b.record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
-    per = [a.elapsed_time(b) for a, b in ev]
-    return total, sum(per) / len(per)
+    return total, total / steps
 
 
 def cpu_baseline(pb, budget_s=12.0):
@@ -175,7 +177,7 @@ def bench_sage(wl, steps, warmup, kv_scale=0.125):
     stream = torch.cuda.current_stream()
     _, pk = time_launches(lambda: pb.run_sage(kv_scale, outs=outs, stream=stream.cuda_stream), steps, warmup, stream)
     nb = algorithmic_bytes(wl, "sage")
-    return {"kernel_us": round(pk * 1e3, 2), "GBs": round(nb / pk / 1e6, 1),
+    return {"us_per_call": round(pk * 1e3, 2), "GBs": round(nb / pk / 1e6, 1),
             "frac_of_peak": round(nb / pk / 1e6 / HBM_PEAK_GBS, 4), "tokens_per_ms": round(wl.B * wl.T / pk, 1)}
 
 
@@ -240,9 +242,9 @@ def bench_block_ops(steps, warmup, rotate=8):
 
     _, prr = time_launches(rr, steps, warmup, stream)
     bsw, brr = N * F * 6, Nr * C * 10
-    return {"swiglu": {"shape": [N, 2 * F], "kernel_us": round(psw * 1e3, 2), "GBs": round(bsw / psw / 1e6, 1),
+    return {"swiglu": {"shape": [N, 2 * F], "us_per_call": round(psw * 1e3, 2), "GBs": round(bsw / psw / 1e6, 1),
                        "frac_of_peak": round(bsw / psw / 1e6 / HBM_PEAK_GBS, 4), "buffer_sets_rotated": rotate},
-            "scaled_residual": {"shape": [Nr, C], "kernel_us": round(prr * 1e3, 2), "GBs": round(brr / prr / 1e6, 1),
+            "scaled_residual": {"shape": [Nr, C], "us_per_call": round(prr * 1e3, 2), "GBs": round(brr / prr / 1e6, 1),
                                 "frac_of_peak": round(brr / prr / 1e6 / HBM_PEAK_GBS, 4),
                                 "buffer_sets_rotated": rotate}}
 
@@ -264,7 +266,7 @@ def pmc_summary(root):
         assert vals, (d, key)
         return sum(vals) / len(vals), len(vals)
 
-    kern = "qk_kernel<64, 1, 0, 1, 0>"
+    kern = "qk_kernel<64, 1, 0, 1, 0, 8, 0>"
     fk, nf = per_dispatch("pmc_FETCH_SIZE", kern)
     wk, nw = per_dispatch("pmc_WRITE_SIZE", kern)
     cf, _ = per_dispatch("pmccopy_FETCH_SIZE", "copyBuffer")
@@ -366,11 +368,12 @@ def main():
                      "kernel_us": round(r["kernel_ms"] * 1e3, 2)},
     }
     if args.extra:
-        extra = {}
+        extra = {"note": "us_per_call: average over back-to-back calls of the timed region (a call may launch "
+                          "a clear and a total kernel around the main one)"}
         for name, rot in (("tile", 8), ("tiles8", 1)):
             w = synth.workloads()[name]
             _, rr = bench_store(w, max(10, args.steps // 2), args.warmup, rotate=rot)
-            extra[name] = {"kernel_us": round(rr["kernel_ms"] * 1e3, 2),
+            extra[name] = {"us_per_call": round(rr["kernel_ms"] * 1e3, 2),
                            "GBs": round(rr["bytes"] / rr["kernel_ms"] / 1e6, 1),
                            "frac_of_peak": round(rr["bytes"] / rr["kernel_ms"] / 1e6 / HBM_PEAK_GBS, 4),
                            "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
