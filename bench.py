@@ -72,9 +72,24 @@ def time_launches(launch, steps, warmup, stream):
     return total, total / steps
 
 
+def host_cpu() -> str:
+    """The host CPU model and the number of CPUs this process may use."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return f"{model}, {n} CPUs available to the process"
+
+
 def cpu_baseline(pb, budget_s=12.0):
-    """The oracle (plain single-threaded C) on the first tokens of the same workload, growing the
-    sample until about budget_s seconds of CPU work."""
+    """The oracle (plain single-threaded C) on the first tokens of the same workload: a short
+    calibration run, then one run sized to about budget_s seconds of CPU work."""
     import dataclasses
 
     import oracle
@@ -82,20 +97,27 @@ def cpu_baseline(pb, budget_s=12.0):
     wl = pb.wl
     x = pb.qkv_host()
     oracle.lib()
-    ts, spent, tokens = 4096, 0.0, 0
-    while True:
+
+    def run(ts):
         sub = dataclasses.replace(wl, T=ts, valid=[ts] * wl.B)
         t = time.perf_counter()
         oracle.qk_rmsnorm_rope_permute(oracle_spec(sub), x[:, :ts], wl.in_dtype, pb.wq_host, pb.wk_host, "f32", "f16")
-        dt = time.perf_counter() - t
-        spent, tokens = dt, ts
-        if dt >= budget_s / 3 or ts >= wl.T:
-            break
-        ts = min(wl.T, int(ts * max(2.0, budget_s / 3 / max(dt, 1e-3))))
+        return time.perf_counter() - t
+
+    ts = min(wl.T, 2048)
+    dt = run(ts)
+    tokens = min(wl.T, max(ts, int(ts * budget_s / max(dt, 1e-3))))
+    # the whole workload may take less than the budget: repeat it and take the mean
+    runs, total = 0, 0.0
+    while runs == 0 or total < budget_s * 0.8:
+        total += run(tokens)
+        runs += 1
+    spent = total / runs
     sub = dataclasses.replace(wl, T=tokens, valid=[tokens] * wl.B)
     nbytes = algorithmic_bytes(sub, "store")
     return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "tokens_per_ms": round(tokens * wl.B / spent / 1e3, 2), "seconds": round(spent, 2),
+            "tokens_per_ms": round(tokens * wl.B / spent / 1e3, 2), "seconds": round(spent, 2), "runs": runs,
+            "host": host_cpu(),
             "sample": f"first {tokens} of {wl.T} tokens of the {wl.name} workload (all {wl.H} heads, Q f32, K/V f16), "
                       f"single-threaded C oracle"}
 
@@ -334,6 +356,8 @@ def main():
               "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
     import torch
 
     import synth
@@ -378,7 +402,13 @@ def main():
                            "frac_of_peak": round(rr["bytes"] / rr["kernel_ms"] / 1e6 / HBM_PEAK_GBS, 4),
                            "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
                            "buffer_sets_rotated": rot}
+        tiny = synth.workloads()["tiny"]
+        _, rr = bench_store(tiny, max(20, args.steps), args.warmup)
+        extra["tiny"] = {"us_per_call": round(rr["kernel_ms"] * 1e3, 2), "note": "launch-bound: latency"}
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
+        shard = dataclasses.replace(synth.workloads()["fp8long"], T=13056, valid=[13056])
+        extra["fp8long_shard8"] = bench_fp8(shard, max(10, args.steps // 2), args.warmup)
+        extra["fp8long_shard8"]["note"] = "one of 8 sequence shards (T = 13,056), uncounted"
         extra["sage_latent"] = bench_sage(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra["tensor_latent_k"] = bench_tensor(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra.update(bench_block_ops(max(20, args.steps), args.warmup))

@@ -75,18 +75,13 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
     const uint16_t *tokb = p.qkv + (int64_t)b * p.batch_stride + (int64_t)tg * 8 * p.row_stride;
     const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
     uint32_t r[HPW][M][W / 2];
+    // every slot loads (an absent head of a head count that is not a multiple of 4 re-reads the last
+    // head; its rows are never stored): no branch between the loads
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        if (u < nh) {
-            const uint32_t hd = (uint32_t)(h0 + u) * D;
+        const uint32_t hd = (uint32_t)min(h0 + u, p.H - 1) * D;
 #pragma unroll
-            for (int m = 0; m < M; ++m) load_chunk<W>(tokb + (tlane + hd + 8 * W * m + W * c), r[u][m]);
-        } else {  // absent head of a head count that is not a multiple of 4: zeros, never stored
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int k = 0; k < W / 2; ++k) r[u][m][k] = 0u;
-        }
+        for (int m = 0; m < M; ++m) load_chunk<W>(at16(tokb, tlane + hd + 8 * W * m + W * c), r[u][m]);
     }
 
     // 2. normalise and rotate (Q, K) or take the values as they are (V)
@@ -205,29 +200,26 @@ __device__ __forceinline__ void tensor_amax_fetch(const QkParams &p, int64_t ite
     const uint32_t bgi = it32 / (uint32_t)p.head_chunks;
     const int hc = (int)(it32 - bgi * (uint32_t)p.head_chunks);
     const uint32_t b32 = bgi / (uint32_t)p.groups;
-    it.b = (int)b32;
-    it.i = (int)(bgi - b32 * (uint32_t)p.groups) * 8 + g;
+    // item is the same in every lane: so are b and the token group (made explicit for the compiler)
+    const int b = __builtin_amdgcn_readfirstlane((int)b32);
+    const int tg = __builtin_amdgcn_readfirstlane((int)(bgi - b32 * (uint32_t)p.groups));
+    it.b = b;
+    it.i = tg * 8 + g;
     it.h0 = hc * HPW;
     it.nh = min(HPW, p.H - it.h0);
     if (it.i >= p.T || it.i >= p.vlen[it.b]) return;
     it.live = true;
-    const uint16_t *tok = p.qkv + (int64_t)it.b * p.batch_stride + (int64_t)it.i * p.row_stride;
+    const uint16_t *tokb = p.qkv + (int64_t)b * p.batch_stride + (int64_t)tg * 8 * p.row_stride;
+    const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
+    // every slot loads (an absent head re-reads the last head): no branch between the loads
 #pragma unroll
-    for (int u = 0; u < HPW; ++u)
+    for (int u = 0; u < HPW; ++u) {
+        const uint32_t h = (uint32_t)min(it.h0 + u, p.H - 1);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if (u < it.nh) {
-                load_chunk<W>(tok + (int64_t)(it.h0 + u) * D + 8 * W * m + W * c, it.r[u][m]);
-            } else {
-#pragma unroll
-                for (int k = 0; k < W / 2; ++k) it.r[u][m][k] = 0u;
-            }
-        }
+        for (int m = 0; m < M; ++m) load_chunk<W>(at16(tokb, tlane + h * D + 8 * W * m + W * c), it.r[u][m]);
+    }
 }
 
-// Persistent waves over the work items, the next item's loads in flight while the current one is
-// reduced; one atomic max per block.  Q, K: max |y'| as binary32 bits (NaN above +inf above every
-// finite value); V: max of the 16-bit magnitudes, which order the same way, converted at the end.
 template <int D, int IN, int NN, bool NORM>
 __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
     constexpr int W = 4;
@@ -268,12 +260,14 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
                 }
             } else {
 #pragma unroll
-                for (int u = 0; u < HPW; ++u)
+                for (int u = 0; u < HPW; ++u) {
+                    if (u >= cur.nh) break;
 #pragma unroll
                     for (int m = 0; m < M; ++m)
 #pragma unroll
-                        for (int k = 0; k < W / 2; ++k)  // absent heads hold zeros
+                        for (int k = 0; k < W / 2; ++k)
                             mx = max(mx, max(cur.r[u][m][k] & 0x7FFFu, (cur.r[u][m][k] >> 16) & 0x7FFFu));
+                }
             }
         }
         cur = nxt;

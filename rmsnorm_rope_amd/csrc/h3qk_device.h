@@ -98,6 +98,13 @@ __device__ __forceinline__ int chunk_of_lane(int l) { return l < 4 ? l : 11 - l;
 
 // ------------------------------------------------------------------ loads and stores
 
+// Element e of a wave-uniform 16-bit base, as a 32-bit byte offset (2e < 2^32, which the host's
+// stride limits guarantee): the load then takes the scalar base plus a 32-bit lane offset instead of
+// a 64-bit per-lane address.
+__device__ __forceinline__ const uint16_t *at16(const uint16_t *base, uint32_t e) {
+    return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(base) + e * 2u);
+}
+
 // W consecutive 16-bit values (W = 4: 8 bytes, W = 8: 16 bytes) as W/2 packed words.
 template <int W>
 __device__ __forceinline__ void load_chunk(const uint16_t *p, uint32_t (&r)[W / 2]) {

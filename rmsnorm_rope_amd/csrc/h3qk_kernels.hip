@@ -123,25 +123,20 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
     uint32_t rq[HPW][M][W / 2], rk[HPW][M][W / 2];
     u32x4 rv[HPW][VC];
+    // every slot loads (an absent head of an odd head count re-reads the last head; its rows are
+    // never stored): no branch between the loads
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        if (u < nh) {
-            const uint32_t hq = (uint32_t)(h0 + u) * D, hk = (uint32_t)(p.H + h0 + u) * D;
-            const uint32_t hv = (uint32_t)(2 * p.H + h0 + u) * D;
+        const uint32_t h = (uint32_t)min(h0 + u, p.H - 1);
+        const uint32_t hq = h * D, hk = (p.H + h) * D, hv = (2 * p.H + h) * D;
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                load_chunk<W>(tokb + (tlane + hq + 8 * W * m + W * c), rq[u][m]);
-                load_chunk<W>(tokb + (tlane + hk + 8 * W * m + W * c), rk[u][m]);
-            }
-#pragma unroll
-            for (int vc = 0; vc < VC; ++vc)
-                rv[u][vc] = *reinterpret_cast<const u32x4 *>(tokb + (tlane + hv + 64 * vc + 8 * c));
-        } else {  // absent head of an odd head count: zeros (their rows are never stored)
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int k = 0; k < W / 2; ++k) rq[u][m][k] = rk[u][m][k] = 0u;
+        for (int m = 0; m < M; ++m) {
+            load_chunk<W>(at16(tokb, tlane + hq + 8 * W * m + W * c), rq[u][m]);
+            load_chunk<W>(at16(tokb, tlane + hk + 8 * W * m + W * c), rk[u][m]);
         }
+#pragma unroll
+        for (int vc = 0; vc < VC; ++vc)
+            rv[u][vc] = *reinterpret_cast<const u32x4 *>(at16(tokb, tlane + hv + 64 * vc + 8 * c));
     }
     // 2. weights and rotary entries while the loads are in flight
     float wq[M][W], wk[M][W];
@@ -366,29 +361,28 @@ __device__ __forceinline__ void amax_fetch(const QkParams &p, int64_t item, int 
     const uint32_t bgi = it32 / (uint32_t)p.head_chunks;
     const int hc = (int)(it32 - bgi * (uint32_t)p.head_chunks);
     const uint32_t b32 = bgi / (uint32_t)p.groups;
-    it.b = (int)b32;
-    it.i = (int)(bgi - b32 * (uint32_t)p.groups) * 8 + g;
+    // item is the same in every lane: so are b and the token group (made explicit for the compiler)
+    const int b = __builtin_amdgcn_readfirstlane((int)b32);
+    const int tg = __builtin_amdgcn_readfirstlane((int)(bgi - b32 * (uint32_t)p.groups));
+    it.b = b;
+    it.i = tg * 8 + g;
     it.h0 = hc * HPW;
     it.nh = min(HPW, p.H - it.h0);
     if (it.i >= p.T || it.i >= p.vlen[it.b]) return;
     it.live = true;
-    const uint16_t *tok = p.qkv + (int64_t)it.b * p.batch_stride + (int64_t)it.i * p.row_stride;
+    // the wave's first token as a uniform base, the lane's token as a 32-bit offset
+    const uint16_t *tokb = p.qkv + (int64_t)b * p.batch_stride + (int64_t)tg * 8 * p.row_stride;
+    const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
+    // every slot loads (an absent head of an odd head count re-reads the last head, and its row is
+    // never reduced): no branch between the loads, so none of them waits for another
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        const int h = it.h0 + u;
+        const uint32_t h = (uint32_t)min(it.h0 + u, p.H - 1);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            if (u < it.nh) {
-                load_chunk<W>(tok + (int64_t)h * D + 8 * W * m + W * c, it.rq[u][m]);
-                load_chunk<W>(tok + (int64_t)(p.H + h) * D + 8 * W * m + W * c, it.rk[u][m]);
-                if constexpr (VA) load_chunk<W>(tok + (int64_t)(2 * p.H + h) * D + 8 * W * m + W * c, it.rv[u][m]);
-            } else {  // absent head of an odd head count: zeros, never reduced
-#pragma unroll
-                for (int k = 0; k < W / 2; ++k) {
-                    it.rq[u][m][k] = it.rk[u][m][k] = 0u;
-                    if constexpr (VA) it.rv[u][m][k] = 0u;
-                }
-            }
+            load_chunk<W>(at16(tokb, tlane + h * D + 8 * W * m + W * c), it.rq[u][m]);
+            load_chunk<W>(at16(tokb, tlane + (p.H + h) * D + 8 * W * m + W * c), it.rk[u][m]);
+            if constexpr (VA) load_chunk<W>(at16(tokb, tlane + (2 * p.H + h) * D + 8 * W * m + W * c), it.rv[u][m]);
         }
     }
 }
