@@ -1,0 +1,96 @@
+"""The entry points are graph-capturable: every pass is plain kernel launches on the caller's stream
+(the amax and clip-counter clears are kernels, not memset nodes).  A HIP graph holding the store,
+amax, cast, static cast with counters, one-tensor and sage passes is replayed several times, with
+eager work and the outputs overwritten between replays; every replay must reproduce the eager
+results bit for bit."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from synth.problem import DeviceProblem
+from tests.gpu_util import bits, compare_raw
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rmsnorm_rope_amd import _build
+    if _build.stale():
+        _build.build()
+    torch.cuda.set_device(0)
+    yield
+
+
+def test_graph_replays_match_eager():
+    import rmsnorm_rope_amd as h3
+    wl = dataclasses.replace(synth.workloads()["fp8long"], T=203, valid=[190])
+    pb = DeviceProblem(wl, "cuda")
+    wl64 = dataclasses.replace(synth.workloads()["tiles8"], B=2, T=150, valid=[150, 61])
+    pb64 = DeviceProblem(wl64, "cuda")
+    H, D = wl64.H, wl64.D
+    tdesc = h3.make_desc(wl64.B, wl64.T, H, D, wl64.grid, wl64.n, wl64.table_len, pb64.cos, pb64.sin,
+                         pos_offset=pb64.off, valid_len=wl64.valid_len, eps=wl64.eps, row_stride=wl64.stride,
+                         batch_stride=wl64.T * wl64.stride)
+    kptr = pb64.qkv.data_ptr() + 2 * H * D
+    ds = torch.tensor([0.0045, 0.005, 0.0046], dtype=torch.float32, device="cuda")
+
+    def make_outs():
+        return {
+            "store": (pb.out("f32"), pb.out("bf16"), pb.out("bf16")),
+            "amax": torch.empty(2, dtype=torch.float32, device="cuda"),
+            "cast": (pb.out("e4m3"), pb.out("e4m3"), pb.out("bf16"), torch.empty(2, dtype=torch.float32, device="cuda")),
+            "static": (pb.out("e4m3"), pb.out("e4m3"), pb.out("e4m3"),
+                       torch.empty(h3.SAT_WORDS, dtype=torch.int64, device="cuda")),
+            "tensor": torch.empty((wl64.B, wl64.T, H, D), dtype=torch.float16, device="cuda"),
+            "sage": (pb64.out("f32"), pb64.out("f32"), pb64.out("f16")),
+        }
+
+    def run_all(o, stream=None):
+        pb.run_store("f32", "bf16", outs=o["store"], stream=stream)
+        pb.run_amax(o["amax"], stream=stream)
+        pb.run_cast(o["amax"], outs=o["cast"], stream=stream)
+        pb.run_cast_static(ds, v_fp8=True, outs=o["static"], stream=stream)
+        h3.h3_tensor_norm_rope(tdesc, kptr, "f16", pb64.wk, o["tensor"], "f16", h3.LAYOUT_BTHD, stream=stream)
+        pb64.run_sage(0.125, outs=o["sage"], stream=stream)
+
+    def snapshot(o):
+        out = []
+        for v in o.values():
+            for t in (v if isinstance(v, tuple) else (v,)):
+                out.append(bits(t).copy())
+        return out
+
+    eager = make_outs()
+    run_all(eager)
+    torch.cuda.synchronize()
+    ref = snapshot(eager)
+
+    graphed = make_outs()
+    run_all(graphed)  # warm up outside the capture (first-call device queries)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all(graphed)
+    scratch = make_outs()
+    for rep in range(4):
+        for v in graphed.values():  # overwrite every output (and the counter buffer) eagerly
+            for t in (v if isinstance(v, tuple) else (v,)):
+                t.view(torch.uint8).fill_(0xA5)
+        run_all(scratch)  # unrelated eager work on the same stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot(graphed)
+        assert len(got) == len(ref)
+        for i, (a, b) in enumerate(zip(got, ref)):
+            if a.dtype == np.int64:  # the counter buffer: only the counts are defined
+                a, b = a[:3], b[:3]
+            compare_raw(a, b, f"replay {rep} output {i}")
+        print(f"[graph] replay {rep}: {len(got)} outputs bit-identical to eager", flush=True)
