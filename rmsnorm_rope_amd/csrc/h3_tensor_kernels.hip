@@ -118,49 +118,8 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
         if (u >= nh) break;
         const int64_t o = obase + u * p.out_hstride;
         if constexpr (MODE == MODE_CAST) {
-            float q[M][W];
-            bool bad = false;  // a quotient above 448 in magnitude or NaN
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    q[m][k] = quotient(x[u][m][k], ds, rcp);
-                    bad = bad || !(__builtin_fabsf(q[m][k]) <= 448.0f);
-                }
-            // exact: NaN data or an extreme descale; clip: a quotient past the range (saturates)
-            bool exact = !fast, clip = false;
-            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-                bool nan = false;
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k) nan = nan || q[m][k] != q[m][k];
-                exact = exact || __builtin_amdgcn_ballot_w64(nan) != 0;
-                clip = true;
-            }
-            if (exact) {
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k)
-                        if (!fast || !(__builtin_fabsf(q[m][k]) <= 448.0f)) q[m][k] = x[u][m][k] / ds;
-            }
-            if (p.sat && (clip || exact)) {
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k)
-                        nsat += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(q[m][k]) > 448.0f));
-            }
-            if (clip && !exact) {  // no NaN here: saturate ahead of the conversion instruction
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k) q[m][k] = __builtin_amdgcn_fmed3f(q[m][k], -448.0f, 448.0f);
-            }
             uint32_t cw[M][W / 4];
-#pragma unroll
-            for (int m = 0; m < M; ++m) pack_e4m3<W>(q[m], !exact, cw[m]);
+            cast_e4m3_wave<M, W>(x[u], ds, rcp, fast, p.sat != nullptr, nsat, cw);
             if constexpr (W == 8 && M == 2) {
                 store_words_pairs<1, W>(p.q, o + olane, c, cw[0], cw[1]);
             } else {

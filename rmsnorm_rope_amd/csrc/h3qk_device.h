@@ -399,5 +399,57 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// E4M3 codes of the M x W values y / ds of one tensor (ds its descale, rcp = RN(1 / ds), fast: ds
+// within the quotient's checked range), four codes per word.  The quotients are correctly rounded
+// (quotient()); the decisions are wave-uniform: a NaN quotient or a descale outside the checked
+// range sends the whole wave through correctly rounded division and the integer encoder; quotients
+// past 448 are clamped with v_med3 ahead of the conversion instruction.  With count, the quotients
+// past 448 over the wave's active lanes are added to nsat (a wave-uniform value).
+template <int M, int W>
+__device__ __forceinline__ void cast_e4m3_wave(const float (&y)[M][W], float ds, float rcp, bool fast, bool count,
+                                               uint32_t &nsat, uint32_t (&w)[M][W / 4]) {
+    float q[M][W];
+    bool bad = false;  // a quotient above 448 in magnitude or NaN
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            q[m][k] = quotient(y[m][k], ds, rcp);
+            bad = bad || !(__builtin_fabsf(q[m][k]) <= 448.0f);
+        }
+    bool exact = !fast, clip = false;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        bool nan = false;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int k = 0; k < W; ++k) nan = nan || q[m][k] != q[m][k];
+        exact = exact || __builtin_amdgcn_ballot_w64(nan) != 0;
+        clip = true;
+    }
+    if (exact) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                if (!fast || !(__builtin_fabsf(q[m][k]) <= 448.0f)) q[m][k] = y[m][k] / ds;
+    }
+    if (count && (clip || exact)) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                nsat += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(q[m][k]) > 448.0f));
+    }
+    if (clip && !exact) {  // no NaN here
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int k = 0; k < W; ++k) q[m][k] = __builtin_amdgcn_fmed3f(q[m][k], -448.0f, 448.0f);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) pack_e4m3<W>(q[m], !exact, w[m]);
+}
+
 }  // namespace
 }  // namespace h3

@@ -138,6 +138,52 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
         for (int vc = 0; vc < VC; ++vc)
             rv[u][vc] = *reinterpret_cast<const u32x4 *>(at16(tokb, tlane + hv + 64 * vc + 8 * c));
     }
+    // V needs nothing from Q and K: a bit copy (or, for the sage emission, RN16(v * kv_scale)) is
+    // stored as soon as it arrives, which frees its registers before the row arithmetic (measured:
+    // cast 627 -> 609 us on the FP8 long sequence, store 631 -> 623 us on the full latent)
+    uint32_t nsat[3] = {0u, 0u, 0u};  // cast: quotients past the E4M3 range per tensor, this wave
+    if constexpr (VM == 1) {  // V codes with the third descale
+#pragma unroll
+        for (int u = 0; u < HPW; ++u) {
+            if (u >= nh) break;
+            const int64_t o = obase + u * plane;
+            float xv[VC][8];
+#pragma unroll
+            for (int vc = 0; vc < VC; ++vc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t wd = rv[u][vc][e >> 1];
+                    xv[vc][e] = in_to_f32<IN>((e & 1) ? (wd >> 16) : (wd & 0xFFFFu));
+                }
+            uint32_t cv[VC][2];
+            cast_e4m3_wave<VC, 8>(xv, ds[2], rcp[2], fast, p.sat != nullptr, nsat[2], cv);
+            if constexpr (VC == 2) {  // each token's 128-byte row in one instruction
+                store_words_pairs<1, 8>(p.v, o + olane, c, cv[0], cv[1]);
+            } else {  // 8 tokens' 64-byte rows: 512 contiguous bytes
+                st_nt(reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(p.v) + o + (olane + 8 * c)),
+                      (u32x2){cv[0][0], cv[0][1]});
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < HPW; ++u) {
+            if (u >= nh) break;
+            const int64_t o = obase + u * plane;
+#pragma unroll
+            for (int vc = 0; vc < VC; ++vc) {
+                u32x4 w = rv[u][vc];
+                if constexpr (VM == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = keep_f32(in_to_f32<IN>(w[e] & 0xFFFFu) * p.kv_scale);
+                        const float hi = keep_f32(in_to_f32<IN>(w[e] >> 16) * p.kv_scale);
+                        w[e] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+                    }
+                }
+                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)), w);
+            }
+        }
+    }
     // 2. weights and rotary entries while the loads are in flight
     float wq[M][W], wk[M][W];
     load_weights<W, M>(p.wq, c, wq);
@@ -177,108 +223,9 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
         row_scale_rotate<W, M>(xq, rr[2 * u], wq, cs, sn, rot);
         row_scale_rotate<W, M>(xk, rr[2 * u + 1], wk, cs, sn, rot);
         if constexpr (MODE == MODE_CAST) {
-            float qq[2][M][W];
-            float xv[VF8 ? VC : 1][8], qv[VF8 ? VC : 1][8];
-            bool bad = false;  // a quotient above 448 in magnitude or NaN
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    qq[0][m][k] = quotient(xq[m][k], ds[0], rcp[0]);
-                    qq[1][m][k] = quotient(xk[m][k], ds[1], rcp[1]);
-                    bad = bad || !(__builtin_fabsf(qq[0][m][k]) <= 448.0f) || !(__builtin_fabsf(qq[1][m][k]) <= 448.0f);
-                }
-            if constexpr (VF8) {
-#pragma unroll
-                for (int vc = 0; vc < VC; ++vc)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t wd = rv[u][vc][e >> 1];
-                        xv[vc][e] = in_to_f32<IN>((e & 1) ? (wd >> 16) : (wd & 0xFFFFu));
-                        qv[vc][e] = quotient(xv[vc][e], ds[2], rcp[2]);
-                        bad = bad || !(__builtin_fabsf(qv[vc][e]) <= 448.0f);
-                    }
-            }
-            // exact: NaN data or an extreme descale (rare): correctly rounded division where the
-            // quotient is out of the checked range, and the integer encoder, for the whole wave.
-            // clip: some quotient past the range (a descale below the data's amax / 448): it saturates.
-            bool exact = !fast, clip = false;
-            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-                bool nan = false;
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k) nan = nan || qq[0][m][k] != qq[0][m][k] || qq[1][m][k] != qq[1][m][k];
-                if constexpr (VF8) {
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) nan = nan || qv[vc][e] != qv[vc][e];
-                }
-                exact = exact || __builtin_amdgcn_ballot_w64(nan) != 0;
-                clip = true;
-            }
-            if (exact) {
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k) {
-                        if (!fast || !(__builtin_fabsf(qq[0][m][k]) <= 448.0f)) qq[0][m][k] = xq[m][k] / ds[0];
-                        if (!fast || !(__builtin_fabsf(qq[1][m][k]) <= 448.0f)) qq[1][m][k] = xk[m][k] / ds[1];
-                    }
-                if constexpr (VF8) {
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (!fast || !(__builtin_fabsf(qv[vc][e]) <= 448.0f)) qv[vc][e] = xv[vc][e] / ds[2];
-                }
-            }
-            if (p.sat && (clip || exact)) {  // count quotients past the range over the active lanes
-                uint32_t n0 = 0, n1 = 0, n2 = 0;
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k) {
-                        n0 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(qq[0][m][k]) > 448.0f));
-                        n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(qq[1][m][k]) > 448.0f));
-                    }
-                if constexpr (VF8) {
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            n2 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_fabsf(qv[vc][e]) > 448.0f));
-                }
-                if (lane == (int)__builtin_ctzll(__builtin_amdgcn_read_exec())) {
-                    // partial counts spread over slots (one 128-byte line each) to keep atomics apart
-                    unsigned long long *slot = p.sat + 16 * (1 + (blockIdx.x & (H3_SAT_SLOTS - 1)));
-                    if (n0) atomicAdd(slot, (unsigned long long)n0);
-                    if (n1) atomicAdd(slot + 1, (unsigned long long)n1);
-                    if (n2) atomicAdd(slot + 2, (unsigned long long)n2);
-                }
-            }
-            if (clip && !exact) {  // no NaN here: saturate to +-448 ahead of the conversion instruction
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int k = 0; k < W; ++k) {
-                        qq[0][m][k] = __builtin_amdgcn_fmed3f(qq[0][m][k], -448.0f, 448.0f);
-                        qq[1][m][k] = __builtin_amdgcn_fmed3f(qq[1][m][k], -448.0f, 448.0f);
-                    }
-                if constexpr (VF8) {
-#pragma unroll
-                    for (int vc = 0; vc < VC; ++vc)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) qv[vc][e] = __builtin_amdgcn_fmed3f(qv[vc][e], -448.0f, 448.0f);
-                }
-            }
             uint32_t cw[2][M][W / 4];
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                pack_e4m3<W>(qq[0][m], !exact, cw[0][m]);
-                pack_e4m3<W>(qq[1][m], !exact, cw[1][m]);
-            }
+            cast_e4m3_wave<M, W>(xq, ds[0], rcp[0], fast, p.sat != nullptr, nsat[0], cw[0]);
+            cast_e4m3_wave<M, W>(xk, ds[1], rcp[1], fast, p.sat != nullptr, nsat[1], cw[1]);
             if constexpr (W == 8 && M == 2) {
                 store_words_pairs<1, W>(p.q, o + olane, c, cw[0][0], cw[0][1]);
                 store_words_pairs<1, W>(p.k, o + olane, c, cw[1][0], cw[1][1]);
@@ -287,17 +234,6 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 for (int m = 0; m < M; ++m) {
                     store_code_words<W>(p.q, o + (olane + 8 * W * m + W * c), cw[0][m]);
                     store_code_words<W>(p.k, o + (olane + 8 * W * m + W * c), cw[1][m]);
-                }
-            }
-            if constexpr (VF8) {
-                uint32_t cv[VC][2];
-#pragma unroll
-                for (int vc = 0; vc < VC; ++vc) pack_e4m3<8>(qv[vc], !exact, cv[vc]);
-                if constexpr (VC == 2) {  // each token's 128-byte row in one instruction
-                    store_words_pairs<1, 8>(p.v, o + olane, c, cv[0], cv[1]);
-                } else {  // 8 tokens' 64-byte rows: 512 contiguous bytes
-                    st_nt(reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(p.v) + o + (olane + 8 * c)),
-                          (u32x2){cv[0][0], cv[0][1]});
                 }
             }
         } else {
@@ -320,24 +256,14 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                 for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c), xk[m]);
             }
         }
-        if constexpr (VM == 0) {
-#pragma unroll
-            for (int vc = 0; vc < VC; ++vc)
-                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)), rv[u][vc]);
-        } else if constexpr (VM == 2) {  // sage: RN16(RN32(v * kv_scale))
-#pragma unroll
-            for (int vc = 0; vc < VC; ++vc) {
-                uint32_t wv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t wd = rv[u][vc][e];
-                    const float lo = keep_f32(in_to_f32<IN>(wd & 0xFFFFu) * p.kv_scale);
-                    const float hi = keep_f32(in_to_f32<IN>(wd >> 16) * p.kv_scale);
-                    wv[e] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
-                }
-                st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.v) + o + (olane + 64 * vc + 8 * c)),
-                      (u32x4){wv[0], wv[1], wv[2], wv[3]});
-            }
+    }
+    if constexpr (MODE == MODE_CAST) {
+        // partial counts spread over slots (one 128-byte line each) to keep the atomics apart
+        if (p.sat && (nsat[0] | nsat[1] | nsat[2]) && lane == (int)__builtin_ctzll(__builtin_amdgcn_read_exec())) {
+            unsigned long long *slot = p.sat + 16 * (1 + (blockIdx.x & (H3_SAT_SLOTS - 1)));
+            if (nsat[0]) atomicAdd(slot, (unsigned long long)nsat[0]);
+            if (nsat[1]) atomicAdd(slot + 1, (unsigned long long)nsat[1]);
+            if (nsat[2]) atomicAdd(slot + 2, (unsigned long long)nsat[2]);
         }
     }
 }
