@@ -77,6 +77,7 @@ SMALL = [
     ("tiny", dict(row_stride=3 * 2 * 64 + 24)),
     ("tile", dict(T=3000, grid=(31, 16, 16), valid=[2999])),
     ("tiles8", dict(T=257, B=5, valid=[257, 256, 1, 0, 100])),
+    ("tiny", dict(B=64, T=9, grid=(1, 3, 3), valid=[i % 10 for i in range(64)], offset_hw_max=5)),  # max batch
 ]
 
 
@@ -91,6 +92,16 @@ def test_store_small(name, kw):
 def test_store_dtype_matrix(q_dt, k_dt, in_dt):
     check_store(W("tiny", T=40, grid=(2, 4, 5), B=2, valid=[40, 31], in_dtype=in_dt), q_dt, k_dt)
     check_store(W("tiny", T=12, grid=(1, 3, 4), D=128, n=16, in_dtype=in_dt), q_dt, k_dt)
+
+
+def test_store_max_row_stride():
+    """The largest row stride the ABI accepts (2^26 elements): token 8 of a group starts 7 * 2^27
+    bytes past the group's first token, the far end of the 32-bit lane offsets."""
+    wl = W("tiny", T=9, grid=(1, 3, 3), row_stride=1 << 26)
+    x = np.zeros((1, 9, 1 << 26), np.uint16)
+    x[:, :, :3 * wl.H * wl.D] = synth.qkv_host(W("tiny", T=9, grid=(1, 3, 3)))
+    check_store(wl, qkv_bits=x)
+    check_fp8(dataclasses.replace(wl, fp8=True), qkv_bits=x)
 
 
 def test_store_padded_batch_stride():
