@@ -7,8 +7,9 @@
 //   * A work item is 8 consecutive tokens of one item and 2 of its heads.  Lane 8 g + l serves
 //     token g of the 8 and holds, of every head row it touches, the dims
 //     {8W m + W c + k : m < M, k < W} of its chunk c = chunk_of_lane(l), with W = 4, M = 2 for
-//     D = 64 and W = 8, M = 2 for D = 128.  Loads are 8 W contiguous bytes per token per instruction, the f32 Q store of a
-//     D = 64 row is two full 128-byte lines, V moves in 16-byte lanes.
+//     D = 64 and W = 8, M = 2 for D = 128.  Loads are 8 W contiguous bytes per token per
+//     instruction, the f32 Q store of a D = 64 row is two full 128-byte lines, V moves in 16-byte
+//     lanes.  Every address is a wave-uniform base plus a 32-bit lane offset.
 //   * The halving reduction tree maps onto that layout as: levels o >= 8W fold chunks inside
 //     the lane, levels 4W, 2W, W are DPP butterflies across the token's 8 lanes (half-mirror,
 //     then xor 2, then xor 1), levels below W fold inside the chunk.  Floating-point addition is
@@ -18,10 +19,10 @@
 //     x 8 heads.  Blocks are dispatched in order, so the chip writes a narrow sliding window of
 //     each head plane of the [B, H, T, D] outputs; on MI355X that keeps HBM write efficiency
 //     well above a persistent grid-stride sweep, which holds a window of every plane open.
-//     Each wave issues its data loads first, then decodes positions and fetches weights and
-//     rotary entries while the loads are in flight.  Outputs are written once and never read
-//     back, so they bypass the caches (nontemporal stores), each row as whole 128-byte lines.
-//     At most 3 blocks are resident per CU (see kStoreBlocksPerCU).
+//     Each wave issues its data loads first, stores V (which needs nothing from Q and K) as soon
+//     as it arrives, then decodes positions and fetches weights and rotary entries.  Outputs are
+//     written once and never read back, so they bypass the caches (nontemporal stores), each row
+//     as whole 128-byte lines.  At most 3 blocks are resident per CU (see kStoreBlocksPerCU).
 //   * Amax pass: persistent waves over the work items with the next item's loads in flight
 //     while the current one is reduced, one atomic max per block and tensor.  It stores nothing,
 //     so it always takes W = 4 (M = D / 32), which keeps the cross-lane tree levels at 12 DPP adds
