@@ -44,6 +44,21 @@ def test_header_constants_match_binding():
     assert h3.SAT_WORDS == 16 * (h3.SAT_SLOTS + 1)
 
 
+def test_header_is_c99_and_every_entry_point_links(tmp_path):
+    """A plain C99 program includes include/h3qk.h, links against the library and calls every entry
+    point (each fails host validation; no GPU call)."""
+    exe = tmp_path / "abi_check"
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror=implicit-function-declaration", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-o", str(exe),
+           os.path.join(ROOT, "tests", "c", "abi_check.c"), "-L", os.path.dirname(h3.LIB_PATH), "-lh3qk",
+           "-Wl,-rpath," + os.path.dirname(h3.LIB_PATH)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "0 failure(s)" in out.stdout
+
+
 def test_abi_version():
     assert h3.h3_abi_version() == 1
 
