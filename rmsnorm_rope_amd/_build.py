@@ -5,6 +5,8 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,7 +19,7 @@ HEADERS = [os.path.join(ROOT, "include", "h3qk.h"), os.path.join(CSRC, "h3qk_int
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # the numerical contract: no contraction, no fast-math, IEEE denormals, correctly rounded
     # division and square root in device code
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
@@ -28,8 +30,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", LIB + ".tmp", *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,6 +40,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (one hipcc per file), then link the library."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="h3qk_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+            futs = [ex.submit(_run, [HIPCC, *FLAGS, *inc, "-c", "-o", obj, src], verbose)
+                    for src, obj in zip(SOURCES, objs)]
+            for f in futs:
+                f.result()
+        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", LIB + ".tmp", *objs], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
