@@ -298,14 +298,14 @@ def pmc_summary(root):
     rd, wr = fk * fs * 1024, wk * ws * 1024
     lines = [
         "# HBM traffic of the fused store kernel on the full-latent workload, from rocprofv3 --pmc.",
-        "# Commands (repository root R, run from /tmp with TMPDIR=/tmp), one counter per run:",
-        "#   rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE -o run --output-format csv -- "
+        "# Commands (repository root R, output directory OUT, run from /tmp with TMPDIR=/tmp), one counter per run:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE -o run --output-format csv -- "
         "python3 $R/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
-        "#   rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE -o run --output-format csv -- "
+        "#   rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE -o run --output-format csv -- "
         "python3 $R/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
         "#   the same two with -d .../pmccopy_<counter> -- python3 $R/bench.py --copy-calibration "
         "(a 2 GiB device copy: 2 GiB read, 2 GiB written)",
-        "#   python3 bench.py --pmc-summary $R/gpurun_out",
+        "#   python3 bench.py --pmc-summary $OUT",
         f"kernel_sha256_16={kernel_digest()}",
         f"dispatches_fetch={nf}",
         f"dispatches_write={nw}",
