@@ -169,6 +169,36 @@ def test_special_rows():
         x[:, 8, :] = 6e-8                                  # smallest f16 subnormal
     check_store(wl, qkv_bits=_crafted(wl, fill))
     check_store(wl, "bf16", "bf16", qkv_bits=_crafted(wl, fill))
+    # eps = 0: a zero row has 1/rms = 1/0 = inf and every y' = 0 * inf = NaN, on both sides
+    check_store(dataclasses.replace(wl, eps=0.0), qkv_bits=_crafted(wl, fill))
+
+
+def test_special_rows_fp8_and_sage():
+    """The same special rows through the cast (NaN rows, inf, saturation) and the sage emission,
+    with and without eps."""
+    import rmsnorm_rope_amd as h3
+    wl = W("fp8long", T=16, valid=[14], H=2, grid=(1, 4, 4))
+    rng = np.random.default_rng(1)
+
+    def fill(x):
+        x[:, :, :] = rng.standard_normal(x.shape)
+        x[:, 1, :] = 0.0
+        x[:, 2, :] = rng.standard_normal(x.shape[-1]) * 2.0 ** -130   # bf16 subnormals
+        x[:, 3, :] = rng.standard_normal(x.shape[-1]) * 1e30
+        x[:, 4, 7] = np.inf
+        x[:, 5, 300] = np.nan
+        x[:, 6, :] = 0.0
+        x[:, 6, 9::128] = 3.0
+    for eps in (1e-6, 0.0):
+        w = dataclasses.replace(wl, eps=eps)
+        check_fp8(w, qkv_bits=_crafted(w, fill))
+        pb = DeviceProblem(w, "cuda", qkv_bits=_crafted(w, fill))
+        q, k, v = pb.run_sage(0.3)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.qk_sage(oracle_spec(w), pb.qkv_host(), w.in_dtype, pb.wq_host, pb.wk_host, 0.3)
+        compare(bits(q), rq, "f32", "sage Q")
+        compare(bits(k), rk, "f32", "sage K")
+        compare(bits(v), rv, "f16", "sage V")
 
 
 # ----------------------------------------------------------------------------- FP8 amax + cast
