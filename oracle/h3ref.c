@@ -16,8 +16,13 @@
  *     F32 Q and F16 K/V written head-major with the same products, sums and casts.
  *   - TensorRT-LLM PR #21485, Summary and the fused_fp8_qk commit messages: QK-norm + RoPE fused
  *     into one amax pass and one cast pass with per-tensor scales; padded rows (from the
- *     key-padding mask) left out of the amax; the packed QKV row stride.
- * Where the pages leave a step open, the reading taken is written next to the step.
+ *     key-padding mask) left out of the amax; the packed QKV row stride; the static scale table
+ *     and the saturation log; the cast of V; norm_rope_tensor for separately projected tensors.
+ *   - stable-diffusion.cpp PR #19, the sage commit: F32 Q, F32 K * kv_scale, F16 V * kv_scale.
+ *   - vllm-omni PR #6607, "Operations" table, SwiGLU and scaled-residual rows.
+ * Where the pages leave a step open, the reading taken is written next to the step.  Every public
+ * function here is pinned by the tests (closed forms, brute force, library routines, the numpy
+ * twin in twin.py).
  *
  * Arithmetic: IEEE binary32, one rounding per written operation, in the order written.
  * Build with -O2 -ffp-contract=off and without fast-math: no fused multiply-add, no
