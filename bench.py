@@ -10,6 +10,7 @@ of the same workload.  --extra adds the one-tile, eight-tile and FP8 long-sequen
 passes as extra lines of the same object.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -229,6 +230,51 @@ def bench_tensor(wl, steps, warmup):
             "identity_us": round(pv * 1e3, 2), "identity_GBs": round(nb / pv / 1e6, 1)}
 
 
+def bench_qk_tensors_2x1797(steps, warmup, rotate=8):
+    """Q and K as separate [2, 1797, 32, 64] f16 tensors, each normalised and rotated into f16
+    [B, T, H, D] by one one-tensor call (two calls per step): the operator shape of the isolated Q/K
+    RMSNorm + RoPE measurement in the B300 validation comment of the vllm-omni MiniMax-H3 VAE review
+    thread (another machine and its own rotary layout: context only).  Timed twice: on one buffer
+    set (its 59 MB stay in the last-level cache, as in a back-to-back operator loop) and rotating
+    over `rotate` sets (cold).  The grid and n are the generator's choice (the thread gives only
+    the shape)."""
+    import torch
+
+    import rmsnorm_rope_amd as h3
+    import synth
+    from synth.problem import DeviceProblem
+    wl = synth.vae_qk_workload()
+    pb = DeviceProblem(wl, "cuda")
+    H, D, T = wl.H, wl.D, wl.T
+    desc = h3.make_desc(wl.B, T, H, D, wl.grid, wl.n, wl.table_len, pb.cos, pb.sin, pos_offset=pb.off,
+                        valid_len=wl.valid_len, eps=wl.eps, row_stride=H * D, batch_stride=T * H * D)
+    qx = pb.qkv[:, :, :H * D].contiguous()
+    kx = pb.qkv[:, :, H * D:2 * H * D].contiguous()
+    del pb.qkv
+    sets = [(qx, kx, torch.empty_like(qx), torch.empty_like(kx))]
+    for _ in range(rotate - 1):
+        sets.append(tuple(t.clone() for t in sets[0]))
+    stream = torch.cuda.current_stream()
+    res = {"shape": "Q and K each [2, 1797, 32, 64] f16 -> f16 [B, T, H, D]", "grid": list(wl.grid), "n": wl.n}
+    nb = 2 * 2 * qx.numel() * 2
+    for label, nsets in (("hot", 1), ("rotated", rotate)):
+        it = [0]
+
+        def step():
+            q, k, qo, ko = sets[it[0] % nsets]
+            it[0] += 1
+            h3.h3_tensor_norm_rope(desc, q, "f16", pb.wq, qo, "f16", h3.LAYOUT_BTHD,
+                                   stream=stream.cuda_stream)
+            h3.h3_tensor_norm_rope(desc, k, "f16", pb.wk, ko, "f16", h3.LAYOUT_BTHD,
+                                   stream=stream.cuda_stream)
+
+        _, per = time_launches(step, steps, warmup, stream)
+        res[f"{label}_us_per_qk_pair"] = round(per * 1e3, 2)
+        res[f"{label}_GBs"] = round(nb / per / 1e6, 1)
+    res["pages_context_us"] = 28.877
+    return res
+
+
 def bench_block_ops(steps, warmup, rotate=8):
     """SwiGLU on [1797, 2 x 8192] f16 and the scaled residual on [2 x 1797, 2048] (fp32 residual,
     f16 branch, per-channel scale), each with `rotate` buffer sets so the 256 MB MALL holds none."""
@@ -411,6 +457,7 @@ def main():
         extra["fp8long_shard8"]["note"] = "one of 8 sequence shards (T = 13,056), uncounted"
         extra["sage_latent"] = bench_sage(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra["tensor_latent_k"] = bench_tensor(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
+        extra["qk_tensors_2x1797x32x64"] = bench_qk_tensors_2x1797(max(20, args.steps), args.warmup)
         extra.update(bench_block_ops(max(20, args.steps), args.warmup))
         out["extra"] = extra
     if not args.no_cpu_baseline:

@@ -273,6 +273,13 @@ SWIGLU_SHAPE = (1797, 8192)          # (N, F): x is [N, 2F]
 RESIDUAL_SHAPE = (2 * 1797, 2048)    # (N, C)
 
 
+def vae_qk_workload() -> Workload:
+    """Q and K of the same thread's isolated Q/K RMSNorm + RoPE measurement, [2, 1797, 32, 64] f16,
+    each a separate tensor.  The thread gives only the shape: the 3 x 599 x 1 token grid and n = 8
+    rotated pairs per axis are this generator's choice."""
+    return Workload("vae_qk", 2, (3, 599, 1), 1797, 32, 64, 8, "f16", "normal", 3001)
+
+
 def swiglu_input(N: int, F: int, dtype: str = "f16", seed: int = 2000) -> np.ndarray:
     """uint16 bits [N, 2F]: standard normal x 3 (so the gate spans silu's curved region)."""
     idx = np.arange(N * 2 * F, dtype=np.int64)

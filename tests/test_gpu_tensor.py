@@ -222,6 +222,16 @@ def test_tensor_slices_match_fused_on_the_gpu():
     say("[full] tiles8 per-tensor slices match the fused pass")
 
 
+def test_vae_qk_shape_compact_q_and_k():
+    """Q and K as separate compact [2, 1797, 32, 64] f16 tensors into f16 [B, T, H, D], the shape
+    the bench times against the thread's isolated Q/K measurement: every output compared."""
+    wl = synth.vae_qk_workload()
+    pb = DeviceProblem(wl, "cuda")
+    for slot in (0, 1):
+        check_tensor_store(TensorCase(wl, slot, compact=True, pb=pb), "f16", 1)
+    say("[full] vae_qk Q and K match the oracle")
+
+
 def test_full_fp8long_tensor_v_cast():
     wl = synth.workloads()["fp8long"]
     rsat = check_tensor_fp8(TensorCase(wl, 2, compact=False), 1, static_descale=3.0 / 448)
