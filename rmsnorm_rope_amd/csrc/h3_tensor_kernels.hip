@@ -194,7 +194,8 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
 
     float w[M][W];
     if constexpr (NORM) load_weights<W, M>(p.wq, c, w);
-    uint32_t mx = 0u;
+    uint32_t mx = 0u;  // identity: max of |x| 16-bit bits (NaN above +inf above every finite value)
+    MagMax mxn;        // normalised: largest |y'|
 
     TensorAmaxItem<D, W, M, HPW> cur, nxt;
     tensor_amax_fetch(p, wave0, g, c, cur);
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
 #pragma unroll
                     for (int m = 0; m < M; ++m)
 #pragma unroll
-                        for (int k = 0; k < W; ++k) mx = max(mx, __float_as_uint(x[m][k]) & 0x7FFFFFFFu);
+                        for (int k = 0; k < W; k += 2) mxn.add2(x[m][k], x[m][k + 1]);
                 }
             } else {
 #pragma unroll
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
         }
         cur = nxt;
     }
+    if constexpr (NORM) mx = mxn.bits();
     mx = wave_max_u32(mx);
     if constexpr (!NORM) mx = __float_as_uint(in_to_f32<IN>(mx));
     __shared__ uint32_t red[4];
@@ -252,13 +254,8 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
     if (!device_facts(&f, err)) return H3_ELAUNCH;
     if constexpr (MODE == MODE_AMAX) {
         auto kern = tensor_amax_kernel<D, IN, NN, NORM>;
-        static int max_blocks = 0;  // resident blocks per CU of this kernel
-        if (max_blocks == 0 &&
-            (hipOccupancyMaxActiveBlocksPerMultiprocessor(&max_blocks, kern, 256, 0) != hipSuccess || max_blocks <= 0)) {
-            max_blocks = 0;
-            *err = "occupancy query failed";
-            return H3_ELAUNCH;
-        }
+        int max_blocks = 0;  // resident blocks per CU of this kernel
+        if (!resident_blocks(reinterpret_cast<const void *>(kern), f, &max_blocks, err)) return H3_ELAUNCH;
         const int rc = clear_words(reinterpret_cast<uint32_t *>(p.amax), 1, stream, "amax", err);
         if (rc != H3_OK) return rc;
         int64_t blocks = (p.items + 3) / 4;

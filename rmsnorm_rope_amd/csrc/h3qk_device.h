@@ -393,6 +393,26 @@ __device__ __forceinline__ void pack_e4m3(const float (&q)[W], bool hw, uint32_t
     }
 }
 
+// Running largest |y| over binary32 values, kept as the bits of |y| (NaN above +inf above every
+// finite value) without clearing a sign bit per value.  Read as unsigned words, the negative values
+// lie above the positive ones and among themselves in order of magnitude; read as signed words, the
+// positive values lie above the negative ones, again in order of magnitude.  The larger of the two
+// maxima with their sign bits cleared is then the largest magnitude: one three-input max per value
+// and word order instead of a mask and a max.  The starting words are +0 and -0.
+struct MagMax {
+    uint32_t u = 0u;
+    int32_t s = (int32_t)0x80000000u;
+    // written as the three-input max instructions: left to itself the compiler rebuilds the
+    // unrolled chain into a tree of two-input maxima, half again as many instructions
+    __device__ __forceinline__ void add2(float a, float b) {
+        asm("v_max3_u32 %0, %0, %1, %2" : "+v"(u) : "v"(a), "v"(b));
+        asm("v_max3_i32 %0, %0, %1, %2" : "+v"(s) : "v"(a), "v"(b));
+    }
+    __device__ __forceinline__ uint32_t bits() const {
+        return max(u & 0x7FFFFFFFu, (uint32_t)s & 0x7FFFFFFFu);
+    }
+};
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 32; o >= 1; o /= 2) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));

@@ -91,12 +91,18 @@ struct QkParams {
     int32_t vlen[H3_MAX_BATCH];
 };
 
-// Device facts read once per process (all devices of one process are gfx950 parts).
+// Facts of the calling thread's current device, queried on its first use and cached per device
+// (thread-safe).
 struct DeviceFacts {
+    int device = -1;
     int cus = 0;
     int lds_per_cu = 0;
 };
 bool device_facts(DeviceFacts *f, std::string *err);
+
+// Resident 256-thread blocks per CU of `kern` on the device of `f` (hipOccupancy query, cached per
+// kernel and device, thread-safe); false with *err set when the query fails.
+bool resident_blocks(const void *kern, const DeviceFacts &f, int *blocks, std::string *err);
 
 // One launch of `kern` with 256-thread blocks and the parameters by value.
 int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err);

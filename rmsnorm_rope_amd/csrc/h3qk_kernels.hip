@@ -30,6 +30,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "h3qk_device.h"
 #include "h3qk_internal.h"
 
@@ -331,8 +336,8 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
     float wq[M][W], wk[M][W];
     load_weights<W, M>(p.wq, c, wq);
     load_weights<W, M>(p.wk, c, wk);
-    uint32_t mx0 = 0u, mx1 = 0u;  // max of |y'| bits: NaN above +inf above every finite value
-    uint32_t mv = 0u;             // VA: max of |v| 16-bit bits, ordered the same way
+    MagMax mx0, mx1;  // largest |y'| of Q and of K
+    uint32_t mv = 0u;  // VA: max of |v| 16-bit bits (NaN above +inf above every finite value)
 
     AmaxItem<D, W, M, HPW, VA> cur, nxt;
     amax_fetch(p, wave0, g, c, cur);
@@ -355,9 +360,9 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int k = 0; k < W; ++k) {
-                        mx0 = max(mx0, __float_as_uint(xq[m][k]) & 0x7FFFFFFFu);
-                        mx1 = max(mx1, __float_as_uint(xk[m][k]) & 0x7FFFFFFFu);
+                    for (int k = 0; k < W; k += 2) {
+                        mx0.add2(xq[m][k], xq[m][k + 1]);
+                        mx1.add2(xk[m][k], xk[m][k + 1]);
                     }
                 if constexpr (VA) {
 #pragma unroll
@@ -372,11 +377,11 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
     }
     constexpr int NT = VA ? 3 : 2;
     __shared__ uint32_t red[3][4];
-    mx0 = wave_max_u32(mx0);
-    mx1 = wave_max_u32(mx1);
+    const uint32_t m0 = wave_max_u32(mx0.bits());
+    const uint32_t m1 = wave_max_u32(mx1.bits());
     if (lane == 0) {
-        red[0][wv] = mx0;
-        red[1][wv] = mx1;
+        red[0][wv] = m0;
+        red[1][wv] = m1;
     }
     if constexpr (VA) {
         // a 16-bit magnitude maps monotonically (NaN above +inf) to the binary32 bits of its value
@@ -439,20 +444,46 @@ int sat_total(unsigned long long *sat, hipStream_t stream, std::string *err) {
 // ------------------------------------------------------------------ dispatch
 
 bool device_facts(DeviceFacts *f, std::string *err) {
-    static DeviceFacts facts;
-    if (facts.cus == 0) {
-        int dev = 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        *err = "no current HIP device";
+        return false;
+    }
+    static std::mutex mu;
+    static std::vector<DeviceFacts> cache;  // by device id; cus == 0: not queried yet
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= cache.size()) cache.resize((size_t)dev + 1);
+    DeviceFacts &c = cache[(size_t)dev];
+    if (c.cus == 0) {
         DeviceFacts t;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        t.device = dev;
+        if (hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipDeviceGetAttribute(&t.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
             t.cus <= 0 || t.lds_per_cu <= 0) {
-            *err = "device query failed (no HIP device?)";
+            *err = "device query failed";
             return false;
         }
-        facts = t;
+        c = t;
     }
-    *f = facts;
+    *f = c;
+    return true;
+}
+
+bool resident_blocks(const void *kern, const DeviceFacts &f, int *blocks, std::string *err) {
+    static std::mutex mu;
+    static std::map<std::pair<const void *, int>, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(kern, f.device);
+    auto it = cache.find(key);
+    if (it == cache.end()) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n <= 0) {
+            *err = "occupancy query failed";
+            return false;
+        }
+        it = cache.emplace(key, n).first;
+    }
+    *blocks = it->second;
     return true;
 }
 
@@ -486,13 +517,8 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
     if (!device_facts(&f, err)) return H3_ELAUNCH;
     if constexpr (MODE == MODE_AMAX) {
         auto kern = qk_amax_kernel<D, IN, NN, VF8>;
-        static int max_blocks = 0;  // resident blocks per CU of this kernel
-        if (max_blocks == 0 &&
-            (hipOccupancyMaxActiveBlocksPerMultiprocessor(&max_blocks, kern, 256, 0) != hipSuccess || max_blocks <= 0)) {
-            max_blocks = 0;
-            *err = "occupancy query failed";
-            return H3_ELAUNCH;
-        }
+        int max_blocks = 0;  // resident blocks per CU of this kernel
+        if (!resident_blocks(reinterpret_cast<const void *>(kern), f, &max_blocks, err)) return H3_ELAUNCH;
         const int rc = clear_words(reinterpret_cast<uint32_t *>(p.amax), VF8 ? 3 : 2, stream, "amax", err);
         if (rc != H3_OK) return rc;
         // persistent waves, two rounds of resident blocks: one atomic per block and tensor
