@@ -16,7 +16,10 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "h3ref.c")
-LIB = os.path.join(HERE, "liboracle_h3ref.so")
+# H3REF_LIB names a prebuilt substitute library (the mutation test loads deliberately broken
+# builds of h3ref.c through it); it is used as given and never rebuilt.
+LIB_OVERRIDE = os.environ.get("H3REF_LIB")
+LIB = LIB_OVERRIDE or os.path.join(HERE, "liboracle_h3ref.so")
 
 DT = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 NP_DT = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
@@ -24,13 +27,15 @@ NP_DT = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain x86-64 SSE binary32: no FMA, no FTZ)."""
-    if force or not os.path.exists(LIB):
-        tmp = LIB + ".tmp"
-        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB)
-    return LIB
+def build(force: bool = True, src: str = SRC, out: str = None) -> str:
+    """Compile the oracle with gcc (plain x86-64 SSE binary32: no FMA, no FTZ).  `src` / `out`
+    build another copy of the source elsewhere (the mutation test)."""
+    out = out or os.path.join(HERE, "liboracle_h3ref.so")
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, src, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -39,7 +44,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        if not LIB_OVERRIDE and (not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC)):
             build()
         L = ctypes.CDLL(LIB)
         P = ctypes.POINTER(Problem)

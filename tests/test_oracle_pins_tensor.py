@@ -120,6 +120,44 @@ def test_v_amax_and_codes_brute_force(name, kw):
         assert not v[b, :, vl:].any()
 
 
+def _put(x, wl, b, i, e, val):
+    """Write val (binary32) into element e of token i of item b, encoded in the input dtype."""
+    enc = (np.array([val], np.float16).view(np.uint16) if wl.in_dtype == "f16"
+           else oracle.encode(np.array([val], F), "bf16"))
+    x[b, i, e] = enc[0]
+
+
+@pytest.mark.parametrize("in_dtype", ["f16", "bf16"])
+def test_amax_planted_maxima_and_nan(in_dtype):
+    """Planted values decide each amax: V's maximum |v| is a planted 7.5 (K holds a planted 6.0,
+    so reading the wrong heads shows), a planted value in a padding row is ignored, and a NaN in
+    one Q row (or one V element) makes that tensor's amax NaN while the others stay finite."""
+    wl = W("tiles8", B=2, T=40, valid=[40, 21], grid=(1, 5, 8), in_dtype=in_dtype)
+    sp, x, wq, wk = _problem(wl)
+    x = x.copy()
+    H, D = wl.H, wl.D
+    _put(x, wl, 1, 5, 2 * H * D + 3 * D + 17, -7.5)   # V, item 1, valid token
+    _put(x, wl, 0, 9, H * D + 2 * D + 1, 6.0)         # K
+    _put(x, wl, 1, 30, 2 * H * D + 5, 9.0)            # V in a padding row of item 1
+    am = oracle.qkv_amax(sp, x, in_dtype, wq, wk)
+    assert am[2] == np.float32(7.5)
+    assert np.isfinite(am).all()
+    xq = x.copy()
+    _put(xq, wl, 0, 3, 4 * D + 2, np.nan)              # one Q element: its row's y' is all NaN
+    aq = oracle.qkv_amax(sp, xq, in_dtype, wq, wk)
+    assert np.isnan(aq[0]) and aq[1] == am[1] and aq[2] == am[2]
+    assert np.isnan(oracle.qk_amax(sp, xq, in_dtype, wq, wk)[0])
+    xv = x.copy()
+    _put(xv, wl, 0, 0, 2 * H * D, np.nan)
+    av = oracle.qkv_amax(sp, xv, in_dtype, wq, wk)
+    assert np.isnan(av[2]) and av[0] == am[0] and av[1] == am[1]
+    xp = x.copy()
+    _put(xp, wl, 1, 35, 0, np.nan)                      # NaN in a padding row: ignored
+    assert np.array_equal(oracle.qkv_amax(sp, xp, in_dtype, wq, wk), am)
+    ts = _tensor_spec(sp)
+    assert np.isnan(oracle.tensor_amax(ts, xq.reshape(-1), in_dtype, wq))
+
+
 def test_tensor_cast_against_its_own_f32_output():
     """Codes of the per-tensor cast are the twin's E4M3 encoding of (f32 output / descale), with
     the descale closed form amax / 448, the static guard, and the clip count from numpy."""
