@@ -73,6 +73,18 @@ def time_launches(launch, steps, warmup, stream):
     return total, total / steps
 
 
+def time_interleaved(launches, steps, warmup, stream, rounds=3):
+    """Time each of several passes (name -> launch) with time_launches, the passes taken in turn
+    and the whole sequence repeated `rounds` times; returns name -> median ms per launch.  The
+    part's clock drifts under sustained load, so passes compared with one another are timed
+    alternately rather than one after the other."""
+    per = {name: [] for name in launches}
+    for _ in range(rounds):
+        for name, fn in launches.items():
+            per[name].append(time_launches(fn, steps, warmup, stream)[1])
+    return {name: sorted(v)[len(v) // 2] for name, v in per.items()}
+
+
 def host_cpu() -> str:
     """The host CPU model and the number of CPUs this process may use."""
     model = "unknown CPU"
@@ -150,8 +162,6 @@ def bench_fp8(wl, steps, warmup):
     amax = torch.empty(2, dtype=torch.float32, device="cuda")
     outs = (pb.out("e4m3"), pb.out("e4m3"), pb.out(wl.in_dtype), torch.empty(2, dtype=torch.float32, device="cuda"))
     stream = torch.cuda.current_stream()
-    ta, pa = time_launches(lambda: pb.run_amax(amax, stream=stream.cuda_stream), steps, warmup, stream)
-    tc, pc = time_launches(lambda: pb.run_cast(amax, outs=outs, stream=stream.cuda_stream), steps, warmup, stream)
     ba, bc = algorithmic_bytes(wl, "amax"), algorithmic_bytes(wl, "cast")
     # static descales (no amax pass) with V cast and clip counters: descales at the data's own
     # amax / 448 (a table calibrated on like data: nothing clips), and at about two standard
@@ -163,19 +173,22 @@ def bench_fp8(wl, steps, warmup):
     cal = torch.cat([amax / 448.0, torch.tensor([vmax / 448.0], device="cuda")]).float().contiguous()
     clip = torch.tensor([0.0045, 0.005, 0.0046], dtype=torch.float32, device="cuda")
     souts = (pb.out("e4m3"), pb.out("e4m3"), pb.out("e4m3"), torch.empty(h3.SAT_WORDS, dtype=torch.int64, device="cuda"))
-    _, ps = time_launches(lambda: pb.run_cast_static(cal, v_fp8=True, outs=souts, stream=stream.cuda_stream),
-                          steps, warmup, stream)
-    _, pk = time_launches(lambda: pb.run_cast_static(clip, v_fp8=True, outs=souts, stream=stream.cuda_stream),
-                          steps, warmup, stream)
     bs = algorithmic_bytes(wl, "cast_v8")
     # dynamic recipe with V cast: amax of Q, K and V in one pass, then the cast with V codes
     am3 = torch.empty(3, dtype=torch.float32, device="cuda")
     ds3 = torch.empty(3, dtype=torch.float32, device="cuda")
     vo = pb.out("e4m3")
-    _, pa3 = time_launches(lambda: h3.h3_qkv_amax(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, stream=stream.cuda_stream),
-                           steps, warmup, stream)
-    _, pc3 = time_launches(lambda: h3.h3_qkv_cast_e4m3(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, souts[0], souts[1],
-                                                       vo, ds3, stream=stream.cuda_stream), steps, warmup, stream)
+    sid = stream.cuda_stream
+    t = time_interleaved({
+        "amax": lambda: pb.run_amax(amax, stream=sid),
+        "cast": lambda: pb.run_cast(amax, outs=outs, stream=sid),
+        "static": lambda: pb.run_cast_static(cal, v_fp8=True, outs=souts, stream=sid),
+        "static_clip": lambda: pb.run_cast_static(clip, v_fp8=True, outs=souts, stream=sid),
+        "qkv_amax": lambda: h3.h3_qkv_amax(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, stream=sid),
+        "qkv_cast": lambda: h3.h3_qkv_cast_e4m3(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, souts[0], souts[1],
+                                                vo, ds3, stream=sid),
+    }, steps, warmup, stream)
+    pa, pc, ps, pk, pa3, pc3 = (t[k] for k in ("amax", "cast", "static", "static_clip", "qkv_amax", "qkv_cast"))
     ba3 = algorithmic_bytes(wl, "amax_v")
     return {"qkv_amax_us": round(pa3 * 1e3, 2), "qkv_amax_GBs": round(ba3 / pa3 / 1e6, 1),
             "qkv_cast_us": round(pc3 * 1e3, 2), "qkv_cast_GBs": round(bs / pc3 / 1e6, 1),
@@ -187,7 +200,8 @@ def bench_fp8(wl, steps, warmup):
             "cast_us": round(pc * 1e3, 2), "cast_GBs": round(bc / pc / 1e6, 1),
             "pair_us": round((pa + pc) * 1e3, 2), "pair_GBs": round((ba + bc) / (pa + pc) / 1e6, 1),
             "pair_frac_of_peak": round((ba + bc) / (pa + pc) / 1e6 / HBM_PEAK_GBS, 4),
-            "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1)}
+            "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / (pa + pc), 1),
+            "timing": "median of 3 rounds, the six passes timed in turn in each round"}
 
 
 def bench_sage(wl, steps, warmup, kv_scale=0.125):
@@ -220,14 +234,17 @@ def bench_tensor(wl, steps, warmup):
                         valid_len=wl.valid_len, eps=wl.eps, row_stride=H * D, batch_stride=T * H * D)
     out = torch.empty((wl.B, T, H, D), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
-    _, pk = time_launches(lambda: h3.h3_tensor_norm_rope(desc, kx, "f16", pb.wk, out, "f16", h3.LAYOUT_BTHD,
-                                                         stream=stream.cuda_stream), steps, warmup, stream)
-    _, pv = time_launches(lambda: h3.h3_tensor_norm_rope(desc, kx, "f16", None, out, "f16", h3.LAYOUT_BTHD,
-                                                         stream=stream.cuda_stream), steps, warmup, stream)
+    sid = stream.cuda_stream
+    t = time_interleaved({
+        "k": lambda: h3.h3_tensor_norm_rope(desc, kx, "f16", pb.wk, out, "f16", h3.LAYOUT_BTHD, stream=sid),
+        "v": lambda: h3.h3_tensor_norm_rope(desc, kx, "f16", None, out, "f16", h3.LAYOUT_BTHD, stream=sid),
+    }, steps, warmup, stream)
+    pk, pv = t["k"], t["v"]
     nb = int(wl.valid_len.sum()) * H * D * 2 + wl.B * T * H * D * 2
     return {"shape": [wl.B, T, H, D], "k_norm_rope_us": round(pk * 1e3, 2), "k_GBs": round(nb / pk / 1e6, 1),
             "k_frac_of_peak": round(nb / pk / 1e6 / HBM_PEAK_GBS, 4),
-            "identity_us": round(pv * 1e3, 2), "identity_GBs": round(nb / pv / 1e6, 1)}
+            "identity_us": round(pv * 1e3, 2), "identity_GBs": round(nb / pv / 1e6, 1),
+            "timing": "median of 3 rounds, the two passes timed in turn in each round"}
 
 
 def bench_qk_tensors_2x1797(steps, warmup, rotate=8):
