@@ -44,7 +44,11 @@
  *   - arguments are validated on the host before anything is enqueued: a call that returns an
  *     error has enqueued nothing (all or nothing), and h3_last_error() describes the failure;
  *   - the unsupported cases return H3_EUNSUPPORTED so a caller can keep its own path;
- *   - outputs must not overlap any input or any other output (H3_EALIAS).
+ *   - outputs must not overlap any input or any other output (H3_EALIAS);
+ *   - calls may come from several host threads at once (the per-device caches of device
+ *     attributes and kernel occupancy are lock-protected; the error text is per thread);
+ *   - every pass is a sequence of kernel launches on `stream` (buffers that must start at zero
+ *     are cleared by a kernel, not a memset), so a caller may capture the calls in a HIP graph.
  */
 #ifndef H3QK_H
 #define H3QK_H
@@ -85,7 +89,7 @@ typedef struct {
     int32_t H;                 /* heads (>= 1) */
     int32_t D;                 /* head dim: 64 or 128 */
     int64_t row_stride;        /* elements between consecutive tokens of the fused projection,
-                                  >= 3*H*D, multiple of 8 (16 bytes) */
+                                  >= 3*H*D, <= 2^26, multiple of 8 (16 bytes) */
     int64_t batch_stride;      /* elements between consecutive items, multiple of 8,
                                   >= T*row_stride when B > 1 */
     int32_t grid[3];           /* Gt, Gh, Gw: token i -> (i/(Gh*Gw), (i/Gw)%Gh, i%Gw) */
