@@ -66,3 +66,25 @@ def compare_raw(got, ref, what):
         bad = np.flatnonzero(g.ravel() != r.ravel())
         raise AssertionError(f"{what}: {bad.size} differing elements, first at {bad[:5].tolist()}: "
                              f"got {g.ravel()[bad[:5]].tolist()} ref {r.ravel()[bad[:5]].tolist()}")
+
+
+def build_c_e2e(out_dir):
+    """Compile tests/c/e2e_gpu.c (plain C99 with gcc) against the HIP runtime, libh3qk and the
+    oracle library; returns the executable's path."""
+    import os
+    import subprocess
+
+    import oracle
+    import rmsnorm_rope_amd as h3
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    oracle_lib = oracle.build(force=False)
+    libdirs = [os.path.dirname(h3.LIB_PATH), os.path.dirname(oracle_lib), "/opt/rocm/lib"]
+    exe = os.path.join(str(out_dir), "e2e_gpu")
+    cmd = ["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror=implicit-function-declaration",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+           os.path.join(root, "tests", "c", "e2e_gpu.c"), "-o", exe,
+           "-L", libdirs[0], "-lh3qk", "-L", libdirs[1], "-loracle_h3ref", "-L", libdirs[2], "-lamdhip64",
+           "-Wl,-rpath," + ":".join(libdirs), "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return exe

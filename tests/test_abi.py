@@ -59,6 +59,12 @@ def test_header_is_c99_and_every_entry_point_links(tmp_path):
     assert "0 failure(s)" in out.stdout
 
 
+def test_c_end_to_end_program_builds(tmp_path):
+    """The pure-C GPU program (tests/c/e2e_gpu.c, run by the gpu tests) compiles and links here."""
+    from tests.gpu_util import build_c_e2e
+    assert os.path.exists(build_c_e2e(tmp_path))
+
+
 def test_abi_version():
     assert h3.h3_abi_version() == 1
 
