@@ -1,7 +1,8 @@
-"""A seeded stress matrix of 256 small cases through the C ABI, every output bit-exact against the
-oracle: D in {64, 128} x input f16/bf16 x T in {1, 7, 32, 33, 1797} x H in {1, 2, 16, 24}, item
-offsets and valid lengths, output dtypes, and row distributions (normal, x20 outliers, binary16 /
-bfloat16 subnormal rows, constant rows, one-hot rows, all-zero rows).  Every fourth case also runs
+"""A seeded stress matrix of small cases (256 by default; --stress-cases N runs N) through the C ABI,
+every output bit-exact against the oracle: D in {64, 128} x input f16/bf16 x T in {1, 7, 32, 33,
+1797} x H in {1, 2, 16, 24}, item offsets and valid lengths, output dtypes, and row distributions
+(normal, x20 outliers, binary16 / bfloat16 subnormal rows, constant rows, one-hot rows, all-zero
+rows).  Every fourth case also runs
 the FP8 amax + cast pair, every eighth the sage emission."""
 import dataclasses
 
@@ -16,8 +17,6 @@ from tests.gpu_util import bits, compare, compare_raw
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-
-N_CASES = 256
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -82,10 +81,10 @@ def _inputs(wl, dist, rng):
     return x
 
 
-def test_stress_matrix():
-    import rmsnorm_rope_amd as h3
+def test_stress_matrix(request):
+    n_cases = request.config.getoption("--stress-cases")
     counts = {"store": 0, "fp8": 0, "sage": 0}
-    for k in range(N_CASES):
+    for k in range(n_cases):
         wl, dist, q_dt, k_dt, rng = _case(k)
         tag = (f"case {k}: B={wl.B} T={wl.T} H={wl.H} D={wl.D} n={wl.n} in={wl.in_dtype} {wl.dist}/{dist} "
                f"valid={list(wl.valid_len)} eps={wl.eps} q={q_dt} k={k_dt}")
@@ -123,4 +122,4 @@ def test_stress_matrix():
             counts["sage"] += 1
         del pb
     print(f"[stress] {counts}", flush=True)
-    assert counts["store"] == N_CASES
+    assert counts["store"] == n_cases
