@@ -2,8 +2,7 @@
 every output bit-exact against the oracle: D in {64, 128} x input f16/bf16 x T in {1, 7, 32, 33,
 1797} x H in {1, 2, 16, 24}, item offsets and valid lengths, output dtypes, and row distributions
 (normal, x20 outliers, binary16 / bfloat16 subnormal rows, constant rows, one-hot rows, all-zero
-rows).  Every fourth case also runs
-the FP8 amax + cast pair, every eighth the sage emission."""
+rows).  Every fourth case also runs the FP8 amax + cast pair, every eighth the sage emission."""
 import dataclasses
 
 import numpy as np
