@@ -2,7 +2,11 @@
 every output bit-exact against the oracle: D in {64, 128} x input f16/bf16 x T in {1, 7, 32, 33,
 1797} x H in {1, 2, 16, 24}, item offsets and valid lengths, output dtypes, and row distributions
 (normal, x20 outliers, binary16 / bfloat16 subnormal rows, constant rows, one-hot rows, all-zero
-rows).  Every fourth case also runs the FP8 amax + cast pair, every eighth the sage emission."""
+rows).  Every fourth case also runs the FP8 amax + cast pair, another fourth the static-scale cast
+with V codes and clip counters (descales at a quarter, one and three times the data's own scale),
+another fourth a one-tensor pass (random slot, packed or compact input, layout, and store or
+dynamic / static cast); every eighth case the Q/K/V FP8 recipe, and another eighth the sage
+emission."""
 import dataclasses
 
 import numpy as np
@@ -12,6 +16,7 @@ import oracle
 import synth
 from synth.problem import DeviceProblem, oracle_spec
 from tests.gpu_util import bits, compare, compare_raw
+from tests.test_gpu_tensor import TensorCase, check_tensor_fp8, check_tensor_store
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +87,8 @@ def _inputs(wl, dist, rng):
 
 def test_stress_matrix(request):
     n_cases = request.config.getoption("--stress-cases")
-    counts = {"store": 0, "fp8": 0, "sage": 0}
+    import rmsnorm_rope_amd as h3
+    counts = {"store": 0, "fp8": 0, "static": 0, "qkv": 0, "tensor": 0, "sage": 0}
     for k in range(n_cases):
         wl, dist, q_dt, k_dt, rng = _case(k)
         tag = (f"case {k}: B={wl.B} T={wl.T} H={wl.H} D={wl.D} n={wl.n} in={wl.in_dtype} {wl.dist}/{dist} "
@@ -110,6 +116,43 @@ def test_stress_matrix(request):
             compare(bits(k8), ok, "e4m3", f"{tag} K codes")
             compare_raw(bits(v8), ov, f"{tag} V copy")
             counts["fp8"] += 1
+        if k % 4 == 2:  # static descales around the data's own scale, V codes, clip counters
+            ra3 = oracle.qkv_amax(sp, x, wl.in_dtype, pb.wq_host, pb.wk_host)
+            fac = rng.choice([0.25, 1.0, 3.0], 3)
+            ds_h = np.where(np.isfinite(ra3) & (ra3 > 0), ra3 / np.float32(448.0) * fac, 1.0).astype(np.float32)
+            q8, k8, v8, sat = pb.run_cast_static(torch.from_numpy(ds_h).cuda(), v_fp8=True)
+            torch.cuda.synchronize()
+            oq, ok, ov, osat = oracle.qk_cast_e4m3_static(sp, x, wl.in_dtype, pb.wq_host, pb.wk_host, ds_h, v_fp8=True)
+            compare(bits(q8), oq, "e4m3", f"{tag} static Q codes")
+            compare(bits(k8), ok, "e4m3", f"{tag} static K codes")
+            compare(bits(v8), ov, "e4m3", f"{tag} static V codes")
+            assert np.array_equal(sat[:3].cpu().numpy().astype(np.uint64), osat), (tag, sat[:3].tolist(), osat)
+            counts["static"] += 1
+        if k % 8 == 3:  # the Q/K/V recipe: three amaxes, then Q, K and V codes
+            am3 = torch.empty(3, dtype=torch.float32, device="cuda")
+            h3.h3_qkv_amax(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3)
+            q8, k8, v8 = pb.out("e4m3"), pb.out("e4m3"), pb.out("e4m3")
+            ds3 = torch.empty(3, dtype=torch.float32, device="cuda")
+            h3.h3_qkv_cast_e4m3(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3, q8, k8, v8, ds3)
+            torch.cuda.synchronize()
+            ra3 = oracle.qkv_amax(sp, x, wl.in_dtype, pb.wq_host, pb.wk_host)
+            compare(bits(am3), ra3, "f32", f"{tag} qkv amax")
+            oq, ok, ov, ods = oracle.qkv_cast_e4m3(sp, x, wl.in_dtype, pb.wq_host, pb.wk_host, ra3)
+            compare(bits(ds3), ods, "f32", f"{tag} qkv descales")
+            compare(bits(q8), oq, "e4m3", f"{tag} qkv Q codes")
+            compare(bits(k8), ok, "e4m3", f"{tag} qkv K codes")
+            compare(bits(v8), ov, "e4m3", f"{tag} qkv V codes")
+            counts["qkv"] += 1
+        if k % 4 == 3:  # one tensor: a random slot, packed or compact, layout and output
+            slot = int(rng.integers(0, 3))
+            tc = TensorCase(wl, slot, compact=bool(rng.integers(0, 2)), pb=pb)
+            layout = int(rng.integers(0, 2))
+            if rng.random() < 0.5:
+                check_tensor_store(tc, str(rng.choice(["f32", "f16", "bf16"])), layout)
+            else:
+                sd = None if rng.random() < 0.5 else float(rng.choice([0.0045, 0.01, 0.05]))
+                check_tensor_fp8(tc, layout, static_descale=sd)
+            counts["tensor"] += 1
         if k % 8 == 1:
             s = float(rng.choice([0.125, 0.0883883, 2.5]))
             sq, sk, sv = pb.run_sage(s)
