@@ -85,6 +85,34 @@ def time_interleaved(launches, steps, warmup, stream, rounds=3):
     return {name: sorted(v)[len(v) // 2] for name, v in per.items()}
 
 
+def time_graph(launch, calls, replays, warmup=2):
+    """Capture `calls` back-to-back invocations of `launch` (which must take torch's current
+    stream at call time) in one HIP graph, replay it `warmup` times untimed, then `replays` times
+    between two events; returns ms per invocation."""
+    import torch
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()  # first-call work (device queries) outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            launch()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (replays * calls)
+
+
 def host_cpu() -> str:
     """The host CPU model and the number of CPUs this process may use."""
     model = "unknown CPU"
@@ -288,6 +316,15 @@ def bench_qk_tensors_2x1797(steps, warmup, rotate=8):
         _, per = time_launches(step, steps, warmup, stream)
         res[f"{label}_us_per_qk_pair"] = round(per * 1e3, 2)
         res[f"{label}_GBs"] = round(nb / per / 1e6, 1)
+    q, k, qo, ko = sets[0]
+
+    def pair():  # on torch's current stream at call time (the capture stream under capture)
+        h3.h3_tensor_norm_rope(desc, q, "f16", pb.wq, qo, "f16", h3.LAYOUT_BTHD)
+        h3.h3_tensor_norm_rope(desc, k, "f16", pb.wk, ko, "f16", h3.LAYOUT_BTHD)
+
+    g_ms = time_graph(pair, calls=20, replays=10)
+    res["graph_hot_us_per_qk_pair"] = round(g_ms * 1e3, 2)
+    res["graph_note"] = "20 pairs captured in one HIP graph, replayed on one buffer set"
     res["pages_context_us"] = 28.877
     return res
 
@@ -466,8 +503,12 @@ def main():
                            "tokens_per_ms": round(w.B * w.T / rr["kernel_ms"], 1),
                            "buffer_sets_rotated": rot}
         tiny = synth.workloads()["tiny"]
-        _, rr = bench_store(tiny, max(20, args.steps), args.warmup)
-        extra["tiny"] = {"us_per_call": round(rr["kernel_ms"] * 1e3, 2), "note": "launch-bound: latency"}
+        tpb, rr = bench_store(tiny, max(20, args.steps), args.warmup)
+        touts = (tpb.out("f32"), tpb.out("f16"), tpb.out(tiny.in_dtype))
+        g_ms = time_graph(lambda: tpb.run_store("f32", "f16", outs=touts), calls=50, replays=20)
+        extra["tiny"] = {"us_per_call": round(rr["kernel_ms"] * 1e3, 2),
+                         "graph_us_per_call": round(g_ms * 1e3, 2),
+                         "note": "launch-bound: latency; graph_us_per_call: 50 calls captured in one HIP graph"}
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
         shard = dataclasses.replace(synth.workloads()["fp8long"], T=13056, valid=[13056])
         extra["fp8long_shard8"] = bench_fp8(shard, max(10, args.steps // 2), args.warmup)
