@@ -70,6 +70,24 @@ MUTANTS = [
      "                    uint16_t h3ref_f16_encode_f64(double);\n                    v[o] = h3ref_f16_encode_f64(vs);"),
     ("SwiGLU: gate and up swapped", "double s = g / (1.0 + exp(-g));\n            double v = s * u;",
      "double s = u / (1.0 + exp(-u));\n            double v = s * g;"),
+    ("f16 decode: subnormal step 2^-25", "if (E == 0)       v = ldexpf((float)m, -24);",
+     "if (E == 0)       v = ldexpf((float)m, -25);"),
+    ("bf16 encode: NaN not kept quiet", "return (uint16_t)((x >> 16) | 0x40);", "return (uint16_t)(x >> 16);"),
+    ("e4m3 decode: subnormal step 2^-10", "float v = (E == 0) ? ldexpf((float)m, -9)",
+     "float v = (E == 0) ? ldexpf((float)m, -10)"),
+    ("Q/K/V cast: V with the K descale", "h3ref_descale(amax[1]), h3ref_descale(amax[2])}, 0};",
+     "h3ref_descale(amax[1]), h3ref_descale(amax[1])}, 0};"),
+    ("static cast: V descale unguarded", "v_fp8 ? h3ref_static_descale(descale[2]) : 1.0f},",
+     "v_fp8 ? descale[2] : 1.0f},"),
+    ("tensor cast: padding rows cast instead of zeroed",
+     "out[o] = rc == 1 ? 0 : cast_one(y[(int64_t)h * P->D + d], ds, sat);",
+     "out[o] = rc == 1 ? 0x38 : cast_one(y[(int64_t)h * P->D + d], ds, sat);"),
+    ("tensor amax: starts at one", "    *amax = 0.0f;\n", "    *amax = 1.0f;\n"),
+    ("sage: padding rows of K left at one", "if (rc == 1) { q[o] = 0.0f; k[o] = 0.0f; v[o] = 0; continue; }",
+     "if (rc == 1) { q[o] = 0.0f; k[o] = 1.0f; v[o] = 0; continue; }"),
+    ("SwiGLU: sign of the exponent", "double s = g / (1.0 + exp(-g));", "double s = g / (1.0 + exp(g));"),
+    ("residual: per-channel scale ignored", "float t = b * scale[scale_len == 1 ? 0 : c];",
+     "float t = b * scale[0];"),
     ("residual: product and sum rounded once",
      "float t = b * scale[scale_len == 1 ? 0 : c];\n            out[n * C + c] = res[n * C + c] + t;",
      "out[n * C + c] = (float)((double)res[n * C + c] + (double)b * (double)scale[scale_len == 1 ? 0 : c]);"),
