@@ -452,7 +452,7 @@ def main():
         pmc_summary(args.pmc_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (one process, one MI355X); "
+        print("bench.py: the benchmark runs on one GPU only (one process, one MI355X); "
               "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
