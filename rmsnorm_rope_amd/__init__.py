@@ -92,9 +92,17 @@ def lib():
 
 
 def _ptr(x) -> Optional[int]:
+    """Device address of a tensor argument (or an integer address as given).  A tensor must be a
+    contiguous device tensor: the library reads and writes flat memory, and strides other than the
+    descriptor's would silently address the wrong elements."""
     if x is None:
         return None
     if hasattr(x, "data_ptr"):
+        if hasattr(x, "is_contiguous") and not x.is_contiguous():
+            raise ValueError("tensor arguments must be contiguous (token and batch strides go in the descriptor)")
+        dev = getattr(x, "device", None)
+        if dev is not None and getattr(dev, "type", "cuda") != "cuda":
+            raise ValueError(f"tensor arguments must be device tensors, got one on {dev}")
         return x.data_ptr()
     return int(x)
 

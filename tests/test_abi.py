@@ -65,6 +65,21 @@ def test_c_end_to_end_program_builds(tmp_path):
     assert os.path.exists(build_c_e2e(tmp_path))
 
 
+def test_binding_refuses_host_and_strided_tensors():
+    """The binding passes flat device addresses: a host tensor or a non-contiguous view is refused
+    before the library is called."""
+    import torch
+    with pytest.raises(ValueError, match="device tensors"):
+        h3._ptr(torch.zeros(4))
+    class FakeStrided:  # a device tensor that is not contiguous (no GPU needed to model one)
+        device = type("dev", (), {"type": "cuda"})()
+        def is_contiguous(self): return False
+        def data_ptr(self): return BASE
+    with pytest.raises(ValueError, match="contiguous"):
+        h3._ptr(FakeStrided())
+    assert h3._ptr(BASE) == BASE and h3._ptr(None) is None
+
+
 def test_abi_version():
     assert h3.h3_abi_version() == 1
 
