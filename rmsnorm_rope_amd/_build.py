@@ -16,6 +16,9 @@ SOURCES = [os.path.join(CSRC, f) for f in ("h3qk_kernels.hip", "h3_tensor_kernel
                                              "h3qk_api.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "h3qk.h"), os.path.join(CSRC, "h3qk_internal.h"),
            os.path.join(CSRC, "h3qk_device.h")]
+# test-only check kernels over the library's device helpers, built beside their sources
+CHECK_SRC = os.path.join(ROOT, "tests", "hip", "rsqrt_check.hip")
+CHECK_LIB = os.path.join(ROOT, "tests", "hip", "librsqrt_check.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -54,6 +57,9 @@ def build(verbose: bool = False) -> str:
                 f.result()
         _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", LIB + ".tmp", *objs], verbose)
     os.replace(LIB + ".tmp", LIB)
+    if os.path.exists(CHECK_SRC):
+        _run([HIPCC, *FLAGS, *inc, "-shared", "-o", CHECK_LIB + ".tmp", CHECK_SRC], verbose)
+        os.replace(CHECK_LIB + ".tmp", CHECK_LIB)
     return LIB
 
 
@@ -61,7 +67,14 @@ def stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(f) > t for f in SOURCES + HEADERS)
+    if any(os.path.getmtime(f) > t for f in SOURCES + HEADERS):
+        return True
+    if os.path.exists(CHECK_SRC):
+        if not os.path.exists(CHECK_LIB):
+            return True
+        tc = os.path.getmtime(CHECK_LIB)
+        return any(os.path.getmtime(f) > tc for f in [CHECK_SRC] + HEADERS)
+    return False
 
 
 if __name__ == "__main__":

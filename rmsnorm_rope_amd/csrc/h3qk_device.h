@@ -249,10 +249,33 @@ __device__ __forceinline__ float row_sumsq(const float (&x)[M][W]) {
     return a[0][0];
 }
 
-// r = 1 / sqrt(ss * (1/D) + eps): correctly rounded sqrt, then correctly rounded division.
+// RN(1 / RN(sqrt(v))) for v >= 2^-96, +inf or NaN, without the rescaling the compiler's correctly
+// rounded square root applies to tiny inputs: the hardware square root corrected to its correctly
+// rounded neighbour by the signs of the two FMA residuals, then the hardware reciprocal with one
+// FMA Newton step.  Checked bit for bit against 1.0f / sqrtf(v) (both correctly rounded) for every
+// binary32 v in [2^-96, +inf] and every NaN pattern.  (The reciprocal step alone is not correctly
+// rounded where 1/b is subnormal, b >= 2^126; a square root here is at most 2^64.)
+__device__ __forceinline__ float rsqrt_rn_large(float v) {
+    const float s = __builtin_amdgcn_sqrtf(v);
+    const float sdn = __uint_as_float(__float_as_uint(s) - 1u);
+    const float sup = __uint_as_float(__float_as_uint(s) + 1u);
+    const float rdn = __builtin_fmaf(-sdn, s, v);
+    const float rup = __builtin_fmaf(-sup, s, v);
+    float q = rdn <= 0.0f ? sdn : s;
+    q = rup > 0.0f ? sup : q;
+    q = __builtin_isfinite(v) ? q : s;  // +inf and NaN: the hardware result
+    const float y0 = __builtin_amdgcn_rcpf(q);
+    const float e = __builtin_fmaf(-q, y0, 1.0f);
+    const float y1 = __builtin_fmaf(e, y0, y0);
+    return __builtin_isfinite(q) ? y1 : y0;
+}
+
+// r = 1 / sqrt(ss * (1/D) + eps): correctly rounded sqrt, then correctly rounded division.  With
+// eps >= 2^-96 (a kernel-wide condition) v >= eps and the shorter sequence above gives the same bits.
 __device__ __forceinline__ float row_rstd(float ss, float inv_d, float eps) {
     const float ms = ss * inv_d;
     const float v = ms + eps;
+    if (eps >= 0x1p-96f) return rsqrt_rn_large(v);
     const float sq = __builtin_sqrtf(v);
     return 1.0f / sq;
 }
