@@ -97,7 +97,8 @@ typedef struct {
     int32_t valid_len[H3_MAX_BATCH];     /* per-item valid tokens, 0..min(T, Gt*Gh*Gw) */
     int32_t pairs_per_axis;    /* n: rotated pairs per axis, 0 <= 6n <= D */
     int32_t table_len[3];      /* P_t, P_h, P_w: rows of the t, h, w parts of the tables;
-                                  pos_offset[b][a] + grid[a] <= table_len[a] for every item */
+                                  pos_offset[b][a] + grid[a] <= table_len[a] for every item;
+                                  (P_t + P_h + P_w) * n <= 2^30 (else H3_EINVAL) */
     const float *cos_tab;      /* DEVICE fp32 [(P_t + P_h + P_w)][n], axis-major t, h, w;
                                   never read (may be NULL) when n = 0 */
     const float *sin_tab;      /* DEVICE fp32, same layout */

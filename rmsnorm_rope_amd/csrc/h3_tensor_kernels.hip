@@ -33,7 +33,9 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
     const int lane = threadIdx.x & 63;
     const int c = chunk_of_lane(lane & 7);
     const int g = lane >> 3;
-    const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t item0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the cast walks the items from last to first, where the amax pass before it ended
+    const int64_t item = MODE == MODE_CAST ? p.items - 1 - item0 : item0;
 
     float ds = 1.0f, rcp = 1.0f;
     bool fast = true;
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
         fast = ds >= 0x1p-60f && ds <= 0x1p60f;
         if (p.descale && item == 0 && lane == 0) p.descale[0] = ds;
     }
-    if (item >= p.items) return;
+    if (item < 0 || item >= p.items) return;
 
     const uint32_t it32 = (uint32_t)item;  // items < 2^31 (checked on the host)
     const uint32_t bgi = it32 / (uint32_t)p.head_chunks;
@@ -170,12 +172,14 @@ __device__ __forceinline__ void tensor_amax_fetch(const QkParams &p, int64_t ite
     it.live = true;
     const uint16_t *tokb = p.qkv + (int64_t)b * p.batch_stride + (int64_t)tg * 8 * p.row_stride;
     const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
-    // every slot loads (an absent head re-reads the last head): no branch between the loads
+    // every slot loads (an absent head re-reads the last head): no branch between the loads; the
+    // head's start joins the uniform base, the chunk's place in the row is a constant offset
+    const uint32_t lo = tlane + W * c;
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        const uint32_t h = (uint32_t)min(it.h0 + u, p.H - 1);
+        const uint16_t *bh = tokb + (int64_t)min(it.h0 + u, p.H - 1) * D;
 #pragma unroll
-        for (int m = 0; m < M; ++m) load_chunk<W>(at16(tokb, tlane + h * D + 8 * W * m + W * c), it.r[u][m]);
+        for (int m = 0; m < M; ++m) load_chunk<W>(at16(bh, lo) + 8 * W * m, it.r[u][m]);
     }
 }
 
@@ -197,40 +201,47 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
     uint32_t mx = 0u;  // identity: max of |x| 16-bit bits (NaN above +inf above every finite value)
     MagMax mxn;        // normalised: largest |y'|
 
-    TensorAmaxItem<D, W, M, HPW> cur, nxt;
-    tensor_amax_fetch(p, wave0, g, c, cur);
-    for (int64_t item = wave0; item < p.items; item += nwaves) {
-        tensor_amax_fetch(p, item + nwaves, g, c, nxt);  // next item's loads in flight
-        if (cur.live) {
-            if constexpr (NORM) {
-                float cs[M][W / 2], sn[M][W / 2];
-                bool rot[M][W / 2];
-                rotary_entries<W, M, NN>(p, cur.b, cur.i, c, cs, sn, rot);
+    using Item = TensorAmaxItem<D, W, M, HPW>;
+    auto reduce = [&](const Item &it) {
+        if (!it.live) return;
+        if constexpr (NORM) {
+            float cs[M][W / 2], sn[M][W / 2];
+            bool rot[M][W / 2];
+            rotary_entries<W, M, NN>(p, it.b, it.i, c, cs, sn, rot);
 #pragma unroll
-                for (int u = 0; u < HPW; ++u) {
-                    if (u >= cur.nh) break;
-                    float x[M][W];
-                    unpack_row<W, M, IN>(cur.r[u], x);
-                    const float rr = row_rstd(row_sumsq<W, M>(x), inv_d, p.eps);
-                    row_scale_rotate<W, M>(x, rr, w, cs, sn, rot);
+            for (int u = 0; u < HPW; ++u) {
+                if (u >= it.nh) break;
+                float x[M][W];
+                unpack_row<W, M, IN>(it.r[u], x);
+                const float rr = row_rstd(row_sumsq<W, M>(x), inv_d, p.eps);
+                row_scale_rotate<W, M>(x, rr, w, cs, sn, rot);
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
+                for (int m = 0; m < M; ++m)
 #pragma unroll
-                        for (int k = 0; k < W; k += 2) mxn.add2(x[m][k], x[m][k + 1]);
-                }
-            } else {
+                    for (int k = 0; k < W; k += 2) mxn.add2(x[m][k], x[m][k + 1]);
+            }
+        } else {
 #pragma unroll
-                for (int u = 0; u < HPW; ++u) {
-                    if (u >= cur.nh) break;
+            for (int u = 0; u < HPW; ++u) {
+                if (u >= it.nh) break;
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
+                for (int m = 0; m < M; ++m)
 #pragma unroll
-                        for (int k = 0; k < W / 2; ++k)
-                            mx = max(mx, max(cur.r[u][m][k] & 0x7FFFu, (cur.r[u][m][k] >> 16) & 0x7FFFu));
-                }
+                    for (int k = 0; k < W / 2; ++k)
+                        mx = max(mx, max(it.r[u][m][k] & 0x7FFFu, (it.r[u][m][k] >> 16) & 0x7FFFu));
             }
         }
-        cur = nxt;
+    };
+    // two item buffers taking turns (unrolled by two): each item is reduced while the next one's
+    // loads are in flight
+    Item a, b;
+    tensor_amax_fetch(p, wave0, g, c, a);
+    for (int64_t item = wave0; item < p.items; item += 2 * nwaves) {
+        tensor_amax_fetch(p, item + nwaves, g, c, b);
+        reduce(a);
+        if (item + nwaves >= p.items) break;
+        tensor_amax_fetch(p, item + 2 * nwaves, g, c, a);
+        reduce(b);
     }
     if constexpr (NORM) mx = mxn.bits();
     mx = wave_max_u32(mx);

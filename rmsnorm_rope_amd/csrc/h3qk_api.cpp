@@ -76,7 +76,7 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
         }
     }
     const int64_t rows_total = (int64_t)d->table_len[0] + d->table_len[1] + d->table_len[2];
-    if (rows_total * (int64_t)d->pairs_per_axis > INT32_MAX || T * H * D > ((int64_t)1 << 40))
+    if (rows_total * (int64_t)d->pairs_per_axis > ((int64_t)1 << 30) || T * H * D > ((int64_t)1 << 40))
         return fail(H3_EINVAL, "problem too large");
 
     const uintptr_t q0 = reinterpret_cast<uintptr_t>(qkv);

@@ -105,6 +105,12 @@ __device__ __forceinline__ const uint16_t *at16(const uint16_t *base, uint32_t e
     return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(base) + e * 2u);
 }
 
+// Entry e of a wave-uniform binary32 table, as a 32-bit byte offset (4e < 2^32: the host keeps
+// every table under 2^30 entries).
+__device__ __forceinline__ const float *atf32(const float *base, uint32_t e) {
+    return reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + e * 4u);
+}
+
 // W consecutive 16-bit values (W = 4: 8 bytes, W = 8: 16 bytes) as W/2 packed words.
 template <int W>
 __device__ __forceinline__ void load_chunk(const uint16_t *p, uint32_t (&r)[W / 2]) {
@@ -377,9 +383,9 @@ __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, 
             const int axis = NN ? pr / (NN ? NN : 1) : (int)(((float)pr + 0.5f) * p.inv_n);
             const int jj = pr - axis * n;
             const int row = axis == 0 ? row_t : (axis == 1 ? row_h : row_w);
-            const int idx = row * n + jj;
-            cs[m][q] = rot[m][q] ? p.cos_tab[idx] : 1.0f;
-            sn[m][q] = rot[m][q] ? p.sin_tab[idx] : 0.0f;
+            const uint32_t idx = (uint32_t)(row * n + jj);  // < 2^30 (checked on the host)
+            cs[m][q] = rot[m][q] ? *atf32(p.cos_tab, idx) : 1.0f;
+            sn[m][q] = rot[m][q] ? *atf32(p.sin_tab, idx) : 0.0f;
         }
 }
 
@@ -416,24 +422,19 @@ __device__ __forceinline__ void pack_e4m3(const float (&q)[W], bool hw, uint32_t
     }
 }
 
-// Running largest |y| over binary32 values, kept as the bits of |y| (NaN above +inf above every
-// finite value) without clearing a sign bit per value.  Read as unsigned words, the negative values
-// lie above the positive ones and among themselves in order of magnitude; read as signed words, the
-// positive values lie above the negative ones, again in order of magnitude.  The larger of the two
-// maxima with their sign bits cleared is then the largest magnitude: one three-input max per value
-// and word order instead of a mask and a max.  The starting words are +0 and -0.
+// Running largest |y| over binary32 values.  gfx950's three-input IEEE 754-2019 maximum takes
+// both values through its absolute-value source modifiers, so one instruction folds two values in;
+// a NaN operand makes the result NaN (maximum, unlike maxNum, propagates it), +0 and -0 both enter
+// as +0, and subnormal magnitudes are compared as they are (the kernels run with binary32
+// denormals on).  The result is non-negative, so its bits order like its value, NaN above +inf.
 struct MagMax {
-    uint32_t u = 0u;
-    int32_t s = (int32_t)0x80000000u;
-    // written as the three-input max instructions: left to itself the compiler rebuilds the
-    // unrolled chain into a tree of two-input maxima, half again as many instructions
+    float m = 0.0f;
+    // written as the instruction itself: left to itself the compiler may rebuild the unrolled
+    // chain into a tree of two-input maxima
     __device__ __forceinline__ void add2(float a, float b) {
-        asm("v_max3_u32 %0, %0, %1, %2" : "+v"(u) : "v"(a), "v"(b));
-        asm("v_max3_i32 %0, %0, %1, %2" : "+v"(s) : "v"(a), "v"(b));
+        asm("v_maximum3_f32 %0, %0, |%1|, |%2|" : "+v"(m) : "v"(a), "v"(b));
     }
-    __device__ __forceinline__ uint32_t bits() const {
-        return max(u & 0x7FFFFFFFu, (uint32_t)s & 0x7FFFFFFFu);
-    }
+    __device__ __forceinline__ uint32_t bits() const { return __float_as_uint(m) & 0x7FFFFFFFu; }
 };
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -115,6 +115,7 @@ def call(d=None, qkv=BASE, in_dt=h3.F16, wq=BASE + 0x20000000, wk=BASE + 0x21000
     (dict(T=40, valid_len=[33]), "H3_ERANGE"),             # more valid tokens than grid positions
     (dict(pos_offset=[[1, 0, 0]]), "H3_ERANGE"), (dict(pos_offset=[[0, -1, 0]]), "H3_ERANGE"),
     (dict(cos_tab=0), "H3_EINVAL"), (dict(sin_tab=BASE + 2), "H3_EALIGN"),
+    (dict(table_len=(2, 4, (1 << 27) - 5)), "H3_EINVAL"),  # (P_t + P_h + P_w) * n = 2^30 + 8 entries
 ])
 def test_descriptor_validation(kw, code):
     assert call(desc(**kw)).name == code

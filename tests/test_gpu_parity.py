@@ -259,6 +259,46 @@ def test_fp8_zero_and_nan():
     assert np.isnan(ra[0]) and not np.isnan(ra[1])
 
 
+def test_fp8_subnormal_amax():
+    """Q weights of 2^-130 make every Q output y' (and so its amax) a binary32 subnormal, and the
+    descale amax / 448 a subnormal too, below the cast's fast range: the magnitude maximum must
+    compare subnormals as they are, on the fused pass, on the Q/K/V pass and on the one-tensor
+    pass, and the cast takes its exact path."""
+    import rmsnorm_rope_amd as h3
+    wl = W("fp8long", T=24, valid=[21], H=2, grid=(1, 4, 6))
+    pb = DeviceProblem(wl, "cuda")
+    pb.wq_host = (pb.wq_host * np.float32(2.0 ** -130)).astype(np.float32)
+    pb.wq = torch.from_numpy(pb.wq_host).to("cuda")
+    sp, x = oracle_spec(wl), pb.qkv_host()
+    ra = oracle.qk_amax(sp, x, wl.in_dtype, pb.wq_host, pb.wk_host)
+    assert 0.0 < ra[0] < np.float32(2.0 ** -126) and ra[1] > 1.0, ra
+    amax = pb.run_amax()
+    q8, k8, v8, ds = pb.run_cast(amax)
+    am3 = torch.empty(3, dtype=torch.float32, device="cuda")
+    h3.h3_qkv_amax(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, am3)
+    torch.cuda.synchronize()
+    compare(bits(amax), ra, "f32", "amax")
+    compare(bits(am3)[:2], ra, "f32", "Q/K/V pass amax of Q and K")
+    rq, rk, rv, rds = oracle.qk_cast_e4m3(sp, x, wl.in_dtype, pb.wq_host, pb.wk_host, ra)
+    assert 0.0 < rds[0] < np.float32(2.0 ** -126), rds
+    compare(bits(ds), rds, "f32", "descale")
+    compare(bits(q8), rq, "e4m3", "Q codes")
+    compare(bits(k8), rk, "e4m3", "K codes")
+    compare_raw(bits(v8), rv, "V")
+    # the Q heads alone as one tensor
+    H, D = wl.H, wl.D
+    qx = pb.qkv[:, :, :H * D].contiguous()
+    desc = h3.make_desc(wl.B, wl.T, H, D, wl.grid, wl.n, wl.table_len, pb.cos, pb.sin, pos_offset=pb.off,
+                        valid_len=wl.valid_len, eps=wl.eps, row_stride=H * D, batch_stride=wl.T * H * D)
+    ta = torch.empty(1, dtype=torch.float32, device="cuda")
+    h3.h3_tensor_amax(desc, qx, wl.in_dtype, pb.wq, ta)
+    torch.cuda.synchronize()
+    tsp = oracle.spec_from_workload(wl, row_stride=H * D, batch_stride=wl.T * H * D)
+    rt = oracle.tensor_amax(tsp, bits(qx), wl.in_dtype, pb.wq_host)
+    assert rt.view(np.uint32) == ra[:1].view(np.uint32)[0]
+    compare(bits(ta), np.array([rt], np.float32), "f32", "one-tensor amax of Q")
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 
 def _full_store(name):
