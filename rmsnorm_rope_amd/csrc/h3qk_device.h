@@ -261,6 +261,10 @@ __device__ __forceinline__ float row_sumsq(const float (&x)[M][W]) {
 // FMA Newton step.  Checked bit for bit against 1.0f / sqrtf(v) (both correctly rounded) for every
 // binary32 v in [2^-96, +inf] and every NaN pattern.  (The reciprocal step alone is not correctly
 // rounded where 1/b is subnormal, b >= 2^126; a square root here is at most 2^64.)
+// Special inputs need no select: for v = +inf or NaN both residuals are NaN, neither comparison
+// holds and q stays the hardware result; for q = +inf the Newton residual -inf * 0 + 1 is NaN, which
+// the minimum with 1 (IEEE minNum returns the number) turns into 1, so y1 = y0 = +0.  For finite q
+// the residual is below 2^-21 in magnitude and the minimum leaves it alone.
 __device__ __forceinline__ float rsqrt_rn_large(float v) {
     const float s = __builtin_amdgcn_sqrtf(v);
     const float sdn = __uint_as_float(__float_as_uint(s) - 1u);
@@ -269,11 +273,9 @@ __device__ __forceinline__ float rsqrt_rn_large(float v) {
     const float rup = __builtin_fmaf(-sup, s, v);
     float q = rdn <= 0.0f ? sdn : s;
     q = rup > 0.0f ? sup : q;
-    q = __builtin_isfinite(v) ? q : s;  // +inf and NaN: the hardware result
     const float y0 = __builtin_amdgcn_rcpf(q);
-    const float e = __builtin_fmaf(-q, y0, 1.0f);
-    const float y1 = __builtin_fmaf(e, y0, y0);
-    return __builtin_isfinite(q) ? y1 : y0;
+    const float e = __builtin_fminf(__builtin_fmaf(-q, y0, 1.0f), 1.0f);
+    return __builtin_fmaf(e, y0, y0);
 }
 
 // r = 1 / sqrt(ss * (1/D) + eps): correctly rounded sqrt, then correctly rounded division.  With
