@@ -52,7 +52,12 @@ constexpr int kTensorHeads = 4;   // the same for one separately projected tenso
 // Resident blocks per CU of the streaming store / cast kernels (a cap imposed through LDS): 3 for
 // the fused kernels, 4 for the one-tensor kernels, whose waves move fewer bytes each (measured on
 // the full latent's K heads: 3 blocks 234 us, 4 blocks 175 us, 6-8 blocks within 1 % of 4).
-constexpr int kStoreBlocksPerCU = 3;
+// Store / cast blocks: at most 12 resident waves per CU, in blocks of 8 tokens x 8 heads for D = 64
+// (4 waves) and 8 tokens x 4 heads for D = 128 (2 waves), i.e. 12 KiB of 16-bit input per block
+// either way.
+constexpr int kStoreWavesPerCU = 12;
+template <int D>
+constexpr int store_threads() { return D == 64 ? 256 : 128; }
 constexpr int kTensorBlocksPerCU = 4;
 
 // Everything a QK kernel reads, passed by value in the kernel arguments (< 1.5 KiB).
@@ -105,7 +110,8 @@ bool device_facts(DeviceFacts *f, std::string *err);
 bool resident_blocks(const void *kern, const DeviceFacts &f, int *blocks, std::string *err);
 
 // One launch of `kern` with 256-thread blocks and the parameters by value.
-int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err);
+int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err,
+                  int threads = 256);
 
 // Zero n words on the stream (one block).
 int clear_words(uint32_t *a, int n, hipStream_t stream, const char *what, std::string *err);

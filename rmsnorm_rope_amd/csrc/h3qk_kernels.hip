@@ -15,14 +15,15 @@
 //     then xor 2, then xor 1), levels below W fold inside the chunk.  Floating-point addition is
 //     commutative, so the butterfly partner computes the same bits as the tree node, and all
 //     8 lanes end with ss.
-//   * Store and cast passes: one work item per wave, one short-lived 4-wave block per 8 tokens
-//     x 8 heads.  Blocks are dispatched in order, so the chip writes a narrow sliding window of
+//   * Store and cast passes: one work item per wave, one short-lived block per 8 tokens x 8 heads
+//     (D = 64, 4 waves) or 8 tokens x 4 heads (D = 128, 2 waves), 12 KiB of input either way.
+//     Blocks are dispatched in order, so the chip writes a narrow sliding window of
 //     each head plane of the [B, H, T, D] outputs; on MI355X that keeps HBM write efficiency
 //     well above a persistent grid-stride sweep, which holds a window of every plane open.
 //     Each wave issues its data loads first, stores V (which needs nothing from Q and K) as soon
 //     as it arrives, then decodes positions and fetches weights and rotary entries.  Outputs are
 //     written once and never read back, so they bypass the caches (nontemporal stores), each row
-//     as whole 128-byte lines.  At most 3 blocks are resident per CU (see kStoreBlocksPerCU).
+//     as whole 128-byte lines.  At most 12 waves are resident per CU (see kStoreWavesPerCU).
 //   * Amax pass: persistent waves over the work items with the next item's loads in flight
 //     while the current one is reduced, one atomic max per block and tensor.  It stores nothing,
 //     so it always takes W = 4 (M = D / 32), which keeps the cross-lane tree levels at 12 DPP adds
@@ -504,14 +505,15 @@ bool resident_blocks(const void *kern, const DeviceFacts &f, int *blocks, std::s
     return true;
 }
 
-int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err) {
+int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err,
+                  int threads) {
     if (blocks <= 0) return H3_OK;
     if (blocks > 0x7FFFFFFF) {
         *err = "problem too large for one launch";
         return H3_EUNSUPPORTED;
     }
     void *args[] = {&p};
-    const hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, lds, stream);
+    const hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3((unsigned)threads), args, lds, stream);
     if (e != hipSuccess) {
         *err = std::string("kernel launch failed: ") + hipGetErrorString(e);
         return H3_ELAUNCH;
@@ -521,11 +523,14 @@ int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hip
 
 namespace {
 
-// Resident blocks per CU of the store / cast kernels (kStoreBlocksPerCU).  They stream with no
-// reuse, and on MI355X fewer concurrent blocks keep a narrower window of every output plane open in
-// HBM: 3 blocks (12 waves) per CU measured best for the full-latent workload (4-5 within 1 %, 6-7
-// about 7 % slower).  The cap is imposed by reserving a third of the CU's LDS per block (the kernels
-// use none).
+// Launch geometry of the store / cast kernels (store_threads, kStoreWavesPerCU).  They stream with
+// no reuse, and on MI355X fewer and smaller concurrent blocks keep a narrower window of every output
+// plane open in HBM: 12 waves per CU measured best for the full-latent workload (D = 64; 16-20
+// waves within 1 %, 24-28 about 7 % slower), in 4-wave blocks there (2-wave blocks: 632 against
+// 620 us; 1-wave blocks: 652), and in 2-wave blocks for D = 128 (against 4-wave blocks on the FP8
+// long sequence: cast 606 -> 588 us, cast with V codes 613 -> 576 us, 16-bit store 933 -> 917 us).
+// The cap is imposed by reserving the matching share of the CU's LDS per block (the kernels use
+// none).
 
 template <int D, int IN, int QT, int KT, int MODE, int NN, int VM>
 int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
@@ -549,8 +554,10 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
             const int rc = clear_words(reinterpret_cast<uint32_t *>(p.sat), 2 * H3_SAT_WORDS, stream, "clip counter", err);
             if (rc != H3_OK) return rc;
         }
-        const size_t lds = (size_t)(f.lds_per_cu / kStoreBlocksPerCU);
-        const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + 3) / 4, lds, p, stream, err);
+        constexpr int threads = store_threads<D>(), wpb = threads / 64;  // waves (work items) per block
+        const size_t lds = (size_t)(f.lds_per_cu / (kStoreWavesPerCU / wpb));
+        const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + wpb - 1) / wpb, lds, p, stream,
+                                     err, threads);
         if (rc != H3_OK || MODE != MODE_CAST || !p.sat) return rc;
         return sat_total(p.sat, stream, err);
     }
