@@ -91,15 +91,25 @@ def lib():
     return _lib
 
 
+_NOT_CONTIGUOUS = "tensor arguments must be contiguous (token and batch strides go in the descriptor)"
+
+
 def _ptr(x) -> Optional[int]:
     """Device address of a tensor argument (or an integer address as given).  A tensor must be a
     contiguous device tensor: the library reads and writes flat memory, and strides other than the
     descriptor's would silently address the wrong elements."""
     if x is None:
         return None
-    if hasattr(x, "data_ptr"):
+    is_cuda = getattr(x, "is_cuda", None)
+    if is_cuda is not None:  # a torch tensor: the two checks at the cost of three attribute reads
+        if not is_cuda:
+            raise ValueError(f"tensor arguments must be device tensors, got one on {x.device}")
+        if not x.is_contiguous():
+            raise ValueError(_NOT_CONTIGUOUS)
+        return x.data_ptr()
+    if hasattr(x, "data_ptr"):  # another tensor-like object
         if hasattr(x, "is_contiguous") and not x.is_contiguous():
-            raise ValueError("tensor arguments must be contiguous (token and batch strides go in the descriptor)")
+            raise ValueError(_NOT_CONTIGUOUS)
         dev = getattr(x, "device", None)
         if dev is not None and getattr(dev, "type", "cuda") != "cuda":
             raise ValueError(f"tensor arguments must be device tensors, got one on {dev}")

@@ -77,6 +77,16 @@ def test_binding_refuses_host_and_strided_tensors():
         def data_ptr(self): return BASE
     with pytest.raises(ValueError, match="contiguous"):
         h3._ptr(FakeStrided())
+    class FakeStridedTensor:  # the same through the attributes of a torch tensor
+        is_cuda = True
+        def is_contiguous(self): return False
+        def data_ptr(self): return BASE
+    with pytest.raises(ValueError, match="contiguous"):
+        h3._ptr(FakeStridedTensor())
+    FakeStridedTensor.is_contiguous = lambda self: True
+    assert h3._ptr(FakeStridedTensor()) == BASE
+    with pytest.raises(ValueError, match="device tensors"):
+        h3._ptr(torch.zeros(4).t())
     assert h3._ptr(BASE) == BASE and h3._ptr(None) is None
 
 
