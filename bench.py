@@ -294,6 +294,60 @@ def bench_tensor(wl, steps, warmup):
             "timing": "median of 3 rounds, the two passes timed in turn in each round"}
 
 
+def bench_tensor_fp8(wl, steps, warmup):
+    """The FP8 recipe on one separately projected 128-dim tensor: the K heads of the long sequence
+    copied out as a compact bf16 [B, T, H, D] tensor (the asynchronous Ulysses input form); the
+    amax pass, then the cast to E4M3 codes [B, T, H, D] with its dynamic descale, back to back over
+    two input sets taken in turn; and the 16-bit norm + RoPE store of the same tensor."""
+    import torch
+
+    import rmsnorm_rope_amd as h3
+    from synth.problem import DeviceProblem
+    pb = DeviceProblem(wl, "cuda")
+    H, D, T = wl.H, wl.D, wl.T
+    xs = [pb.qkv[:, :, H * D:2 * H * D].contiguous() for _ in range(2)]
+    del pb.qkv
+    desc = h3.make_desc(wl.B, T, H, D, wl.grid, wl.n, wl.table_len, pb.cos, pb.sin, pos_offset=pb.off,
+                        valid_len=wl.valid_len, eps=wl.eps, row_stride=H * D, batch_stride=T * H * D)
+    am = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in xs]
+    ds = [torch.empty(1, dtype=torch.float32, device="cuda") for _ in xs]
+    codes = [torch.empty((wl.B, T, H, D), dtype=torch.uint8, device="cuda") for _ in xs]
+    out = torch.empty((wl.B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    turn = [0]
+
+    def pair():
+        j = turn[0] & 1
+        turn[0] += 1
+        h3.h3_tensor_amax(desc, xs[j], wl.in_dtype, pb.wk, am[j], stream=sid)
+        h3.h3_tensor_cast_e4m3(desc, xs[j], wl.in_dtype, pb.wk, am[j], False, codes[j], h3.LAYOUT_BTHD,
+                               descale=ds[j], stream=sid)
+
+    t = time_interleaved({
+        "pair": pair,
+        "amax": lambda: h3.h3_tensor_amax(desc, xs[0], wl.in_dtype, pb.wk, am[0], stream=sid),
+        "cast": lambda: h3.h3_tensor_cast_e4m3(desc, xs[0], wl.in_dtype, pb.wk, am[0], False, codes[0],
+                                               h3.LAYOUT_BTHD, descale=ds[0], stream=sid),
+        "store": lambda: h3.h3_tensor_norm_rope(desc, xs[0], wl.in_dtype, pb.wk, out, "bf16", h3.LAYOUT_BTHD,
+                                                stream=sid),
+    }, steps, warmup, stream)
+    nv = int(wl.valid_len.sum()) * H * D
+    b_amax = nv * 2
+    b_cast = nv * 2 + wl.B * T * H * D * 1
+    b_store = nv * 2 + wl.B * T * H * D * 2
+    pp, pa, pc, ps = (t[k] for k in ("pair", "amax", "cast", "store"))
+    return {"shape": [wl.B, T, H, D], "pair_us": round(pp * 1e3, 2),
+            "pair_GBs": round((b_amax + b_cast) / pp / 1e6, 1),
+            "pair_frac_of_peak": round((b_amax + b_cast) / pp / 1e6 / HBM_PEAK_GBS, 4),
+            "amax_us": round(pa * 1e3, 2), "amax_GBs": round(b_amax / pa / 1e6, 1),
+            "cast_us": round(pc * 1e3, 2), "cast_GBs": round(b_cast / pc / 1e6, 1),
+            "store_bf16_us": round(ps * 1e3, 2), "store_bf16_GBs": round(b_store / ps / 1e6, 1),
+            "store_bf16_frac_of_peak": round(b_store / ps / 1e6 / HBM_PEAK_GBS, 4),
+            "timing": "median of 3 rounds, the four passes timed in turn in each round; pair = amax then cast "
+                      "back to back, two input sets taken in turn"}
+
+
 def bench_qk_tensors_2x1797(steps, warmup, rotate=8):
     """Q and K as separate [2, 1797, 32, 64] f16 tensors, each normalised and rotated into f16
     [B, T, H, D] by one one-tensor call (two calls per step): the operator shape of the isolated Q/K
@@ -532,6 +586,8 @@ def main():
         shard = dataclasses.replace(synth.workloads()["fp8long"], T=13056, valid=[13056])
         extra["fp8long_shard8"] = bench_fp8(shard, max(10, args.steps // 2), args.warmup)
         extra["fp8long_shard8"]["note"] = "one of 8 sequence shards (T = 13,056), uncounted"
+        extra["fp8long_tensor_k"] = bench_tensor_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2),
+                                                     args.warmup)
         extra["sage_latent"] = bench_sage(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra["tensor_latent_k"] = bench_tensor(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra["qk_tensors_2x1797x32x64"] = bench_qk_tensors_2x1797(max(20, args.steps), args.warmup)
