@@ -395,17 +395,20 @@ __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, 
 // rcp = RN(1 / ds): q0 = RN(y rcp) is within 1.5 ulps of y / ds, one FMA remainder correction makes
 // it faithful, and a second one then gives the correctly rounded quotient (Markstein's theorem on
 // correcting a faithful quotient with a correctly rounded reciprocal; IBM J. Res. Dev. 34(1), 1990).
-// Checked against correctly rounded division for every binary32 y with y / ds in [2^-12, 512) and
-// 80 descales.  The quotient's sign is that of y (ds > 0), which also fixes y = -0.  Quotients
-// below 2^-11 may lose accuracy to underflow in the remainders, but every value under 2^-10
-// encodes to a zero code either way.  The result is a correctly rounded division, so the
-// no-contraction rule of the arithmetic chain is untouched.
+// The remainders are taken negated, e = q ds - y (exact, like y - q ds), and enter the corrections
+// through the FMA's negation modifiers: the values are those of the plain form, and a zero y keeps
+// its sign through every step (-0 + -0 = -0 where the plain form's +0 remainder would give +0), so
+// no sign fix-up follows.  Checked against correctly rounded division for every finite binary32 y
+// and 64 descales: the same bits wherever |y / ds| is in [2^-12, 512), the same E4M3 code below
+// (quotients under 2^-11 may lose accuracy to underflow in the remainders, but every value under
+// 2^-10 encodes to a signed zero code), NaN or past 448 above.  The result is a correctly rounded
+// division, so the no-contraction rule of the arithmetic chain is untouched.
 __device__ __forceinline__ float quotient(float y, float ds, float rcp) {
     const float q0 = y * rcp;
-    const float r0 = __builtin_fmaf(-q0, ds, y);
-    const float q1 = __builtin_fmaf(r0, rcp, q0);
-    const float r1 = __builtin_fmaf(-q1, ds, y);
-    return __builtin_copysignf(__builtin_fmaf(r1, rcp, q1), y);
+    const float e0 = __builtin_fmaf(q0, ds, -y);
+    const float q1 = __builtin_fmaf(-e0, rcp, q0);
+    const float e1 = __builtin_fmaf(q1, ds, -y);
+    return __builtin_fmaf(-e1, rcp, q1);
 }
 
 // Codes of W quotients as W/4 packed words.  hw: the conversion instruction, exact for |q| <= 448
