@@ -237,3 +237,14 @@ def test_full_fp8long_tensor_v_cast():
     rsat = check_tensor_fp8(TensorCase(wl, 2, compact=False), 1, static_descale=3.0 / 448)
     say(f"[full] fp8long V per-tensor static cast clip count {rsat}")
     assert rsat > 0
+
+
+def test_full_fp8long_tensor_k_bthd():
+    """The one-tensor FP8 recipe the bench times, at full size: the FP8 long sequence's K heads as a
+    compact bf16 [1, 104448, 24, 128] tensor; amax, dynamic cast to [B, T, H, D] codes and the
+    16-bit norm + RoPE store, every element against the oracle."""
+    wl = synth.workloads()["fp8long"]
+    tc = TensorCase(wl, 1, compact=True)
+    check_tensor_fp8(tc, 1)
+    check_tensor_store(tc, "bf16", 1)
+    say("[full] fp8long K heads as one tensor: amax, cast and bf16 store match the oracle")
