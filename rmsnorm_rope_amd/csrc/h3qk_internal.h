@@ -53,8 +53,8 @@ constexpr int kTensorHeads = 4;   // the same for one separately projected tenso
 // the fused kernels, 4 for the one-tensor kernels, whose waves move fewer bytes each (measured on
 // the full latent's K heads: 3 blocks 234 us, 4 blocks 175 us, 6-8 blocks within 1 % of 4).
 // Store / cast blocks: at most 12 resident waves per CU, in blocks of 8 tokens x 8 heads for D = 64
-// (4 waves) and 8 tokens x 4 heads for D = 128 (2 waves), i.e. 12 KiB of 16-bit input per block
-// either way.
+// (4 waves) and 8 tokens x 4 heads for D = 128 (2 waves), i.e. 12,288 16-bit input values (24 KiB)
+// per block either way.
 constexpr int kStoreWavesPerCU = 12;
 template <int D>
 constexpr int store_threads() { return D == 64 ? 256 : 128; }

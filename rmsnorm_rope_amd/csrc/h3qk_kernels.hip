@@ -16,7 +16,7 @@
 //     commutative, so the butterfly partner computes the same bits as the tree node, and all
 //     8 lanes end with ss.
 //   * Store and cast passes: one work item per wave, one short-lived block per 8 tokens x 8 heads
-//     (D = 64, 4 waves) or 8 tokens x 4 heads (D = 128, 2 waves), 12 KiB of input either way.
+//     (D = 64, 4 waves) or 8 tokens x 4 heads (D = 128, 2 waves), 24 KiB of input either way.
 //     Blocks are dispatched in order, so the chip writes a narrow sliding window of
 //     each head plane of the [B, H, T, D] outputs; on MI355X that keeps HBM write efficiency
 //     well above a persistent grid-stride sweep, which holds a window of every plane open.
@@ -63,9 +63,10 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     const int c = chunk_of_lane(lane & 7);  // chunk of the row this lane holds
     const int g = lane >> 3;
     const int64_t item0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // The cast walks the items from last to first: the amax pass before it ends on the last ones,
-    // whose lines the last-level cache may still hold (measured on the FP8 long sequence: amax +
-    // cast 831 -> 820 us, the cast alone 602 -> 596 us).  The store pass runs either way alike.
+    // The cast walks the items from last to first, starting where the amax pass before it ends.
+    // Measured on the FP8 long sequence: amax + cast 831 -> 820 us, the cast alone 602 -> 596 us;
+    // the cast costs the same inside the pair as alone, so the gain is the order itself, not lines
+    // left in the last-level cache.  The store pass runs either way alike.
     const int64_t item = MODE == MODE_CAST ? p.items - 1 - item0 : item0;
 
     float ds[3] = {1.0f, 1.0f, 1.0f}, rcp[3] = {1.0f, 1.0f, 1.0f};
