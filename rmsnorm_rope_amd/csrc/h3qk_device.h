@@ -458,14 +458,16 @@ template <int M, int W>
 __device__ __forceinline__ void cast_e4m3_wave(const float (&y)[M][W], float ds, float rcp, bool fast, bool count,
                                                uint32_t &nsat, uint32_t (&w)[M][W / 4]) {
     float q[M][W];
-    bool bad = false;  // a quotient above 448 in magnitude or NaN
+    MagMax qm;  // the lane's largest |quotient| (NaN if any is NaN): one instruction per two values
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int k = 0; k < W; ++k) {
+        for (int k = 0; k < W; k += 2) {
             q[m][k] = quotient(y[m][k], ds, rcp);
-            bad = bad || !(__builtin_fabsf(q[m][k]) <= 448.0f);
+            q[m][k + 1] = quotient(y[m][k + 1], ds, rcp);
+            qm.add2(q[m][k], q[m][k + 1]);
         }
+    const bool bad = !(qm.m <= 448.0f);  // a quotient above 448 in magnitude or NaN
     bool exact = !fast, clip = false;
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
         bool nan = false;
