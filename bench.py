@@ -5,9 +5,10 @@ workload (token grid 62x48x84, T = 249,984, H = 16, D = 64, fp16 fused QKV [1, 2
 Q fp32, K/V fp16 head-major), inputs resident in HBM, launched through the C ABI on torch's
 current stream.  Prints one JSON line: throughput in algorithmic GB/s (read every input element
 once, write every output element once), tokens/ms, the roofline fraction of the fused kernel
-(HIP events around every launch in the timed region) and the CPU oracle timed on a bounded sample
-of the same workload.  --extra adds the one-tile, eight-tile and FP8 long-sequence (amax + cast)
-passes as extra lines of the same object.
+(HIP events on the launch stream around the timed region), the FP8 long-sequence recipe (the amax
+pass then the cast pass, and each alone) under "fp8_pair", and the CPU oracle timed on one host
+thread and on all of them.  --extra adds the one-tile, eight-tile, static-scale, sage, one-tensor
+and decoder-block passes under "extra".
 """
 import argparse
 import dataclasses
@@ -128,39 +129,58 @@ def host_cpu() -> str:
     return f"{model}, {n} CPUs available to the process"
 
 
-def cpu_baseline(pb, budget_s=12.0):
-    """The oracle (plain single-threaded C) on the first tokens of the same workload: a short
-    calibration run, then one run sized to about budget_s seconds of CPU work."""
-    import dataclasses
+def host_threads() -> int:
+    """Host threads for the all-cores oracle run: the CPUs this process may use, at most 16 (one
+    GPU's share of its host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def cpu_baseline(pb, budget_s=10.0):
+    """The oracle (plain C, unchanged) on the same workload, as its token entry point
+    h3ref_qk_tokens_ex run on one host thread and on all of them (disjoint contiguous token blocks,
+    one per thread: rows are independent, so the outputs are the same bits).  The one-thread run
+    takes a prefix of the tokens sized by a short calibration to about budget_s seconds; the
+    all-cores run takes the whole workload, repeated until about budget_s seconds have been spent."""
+    import numpy as np
 
     import oracle
     from synth.problem import algorithmic_bytes, oracle_spec
     wl = pb.wl
-    x = pb.qkv_host()
+    assert wl.B == 1
+    x = pb.qkv_host()[0]
+    sp = oracle_spec(wl)
     oracle.lib()
 
-    def run(ts):
-        sub = dataclasses.replace(wl, T=ts, valid=[ts] * wl.B)
+    def run(ts, threads):
         t = time.perf_counter()
-        oracle.qk_rmsnorm_rope_permute(oracle_spec(sub), x[:, :ts], wl.in_dtype, pb.wq_host, pb.wk_host, "f32", "f16")
+        oracle.qk_tokens_store(sp, x[:ts], np.arange(ts), wl.in_dtype, pb.wq_host, pb.wk_host, "f32", "f16",
+                               threads=threads)
         return time.perf_counter() - t
 
+    def timed(ts, threads):
+        runs, total = 0, 0.0
+        while runs == 0 or total < budget_s * 0.8:
+            total += run(ts, threads)
+            runs += 1
+        spent = total / runs
+        sub = dataclasses.replace(wl, T=ts, valid=[ts])
+        return spent, runs, algorithmic_bytes(sub, "store")
+
     ts = min(wl.T, 2048)
-    dt = run(ts)
-    tokens = min(wl.T, max(ts, int(ts * budget_s / max(dt, 1e-3))))
-    # the whole workload may take less than the budget: repeat it and take the mean
-    runs, total = 0, 0.0
-    while runs == 0 or total < budget_s * 0.8:
-        total += run(tokens)
-        runs += 1
-    spent = total / runs
-    sub = dataclasses.replace(wl, T=tokens, valid=[tokens] * wl.B)
-    nbytes = algorithmic_bytes(sub, "store")
-    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "tokens_per_ms": round(tokens * wl.B / spent / 1e3, 2), "seconds": round(spent, 2), "runs": runs,
-            "host": host_cpu(),
-            "sample": f"first {tokens} of {wl.T} tokens of the {wl.name} workload (all {wl.H} heads, Q f32, K/V f16), "
-                      f"single-threaded C oracle"}
+    dt = run(ts, 1)
+    tok1 = min(wl.T, max(ts, int(ts * budget_s / max(dt, 1e-3))))
+    s1, r1, b1 = timed(tok1, 1)
+    nt = host_threads()
+    sn, rn, bn = timed(wl.T, nt)
+    what = f"tokens of the {wl.name} workload (all {wl.H} heads, Q f32, K/V f16, token-major outputs)"
+    return {"value": round(bn / sn / 1e9, 3), "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "tokens_per_ms": round(wl.T / sn / 1e3, 2), "seconds": round(sn, 3), "runs": rn, "host": host_cpu(),
+            "sample": f"all {wl.T} {what}, {nt} host threads on disjoint token blocks, each running the C "
+                      f"oracle's token entry point",
+            "single_thread": {"value": round(b1 / s1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "tokens_per_ms": round(tok1 / s1 / 1e3, 2), "seconds": round(s1, 2), "runs": r1,
+                              "sample": f"first {tok1} of {wl.T} {what}, one host thread"}}
 
 
 def bench_store(wl, steps, warmup, rotate=1):
@@ -249,6 +269,52 @@ def bench_fp8(wl, steps, warmup):
             "timing": "median of 3 rounds, the seven passes timed in turn in each round; pair = amax then "
                       "cast back to back, two input sets taken in turn; amax_plus_cast = the sum of the "
                       "two passes timed alone"}
+
+
+def bench_fp8_pair(wl, steps, warmup):
+    """The dynamic FP8 recipe as a caller runs it on the long-sequence workload: the amax pass then
+    the cast pass (Q/K E4M3 codes with their descales, V a bf16 copy), back to back on the same
+    input, over two input sets taken in turn so that no amax pass starts on lines the pass before
+    it left in the last-level cache; and each pass alone.  Medians of three rounds, the three timed
+    in turn."""
+    import torch
+
+    from synth.problem import DeviceProblem, algorithmic_bytes
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    sets = []
+    for _ in range(2):
+        pb = DeviceProblem(wl, "cuda")
+        amax = torch.empty(2, dtype=torch.float32, device="cuda")
+        outs = (pb.out("e4m3"), pb.out("e4m3"), pb.out(wl.in_dtype), torch.empty(2, dtype=torch.float32, device="cuda"))
+        sets.append((pb, amax, outs))
+    turn = [0]
+
+    def pair():
+        p_, a_, o_ = sets[turn[0] & 1]
+        turn[0] += 1
+        p_.run_amax(a_, stream=sid)
+        p_.run_cast(a_, outs=o_, stream=sid)
+
+    pb, amax, outs = sets[0]
+    t = time_interleaved({"pair": pair, "amax": lambda: pb.run_amax(amax, stream=sid),
+                          "cast": lambda: pb.run_cast(amax, outs=outs, stream=sid)}, steps, warmup, stream)
+    ba, bc = algorithmic_bytes(wl, "amax"), algorithmic_bytes(wl, "cast")
+    pp, pa, pc = t["pair"], t["amax"], t["cast"]
+    return {"workload": "FP8 long sequence: T=104448 (104076 valid, grid 31x34x99), H=24, D=128, bf16 fused QKV "
+                        "[1,104448,9216] -> Q/K E4M3 codes head-major with descales, V bf16",
+            "pair_us": round(pp * 1e3, 2), "pair_GBs": round((ba + bc) / pp / 1e6, 1),
+            "pair_frac_of_peak": round((ba + bc) / pp / 1e6 / HBM_PEAK_GBS, 4),
+            "valid_tokens_per_ms": round(int(wl.valid_len.sum()) / pp, 1),
+            "amax_us": round(pa * 1e3, 2), "amax_GBs": round(ba / pa / 1e6, 1),
+            "amax_frac_of_peak": round(ba / pa / 1e6 / HBM_PEAK_GBS, 4),
+            "cast_us": round(pc * 1e3, 2), "cast_GBs": round(bc / pc / 1e6, 1),
+            "cast_frac_of_peak": round(bc / pc / 1e6 / HBM_PEAK_GBS, 4),
+            "bytes_amax": ba, "bytes_cast": bc,
+            "kernels": {"amax": "qk_amax_kernel<D=128, bf16> (after a one-block clear of amax[2])",
+                        "cast": "qk_kernel<D=128, bf16 -> E4M3, cast>"},
+            "timing": "HIP events on the launch stream; median of 3 rounds, the pair, the amax pass and the cast "
+                      "pass timed in turn; pair = amax then cast back to back over two input sets taken in turn"}
 
 
 def bench_sage(wl, steps, warmup, kv_scale=0.125):
@@ -565,8 +631,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "qk_kernel<D=64, f16 -> f32/f16, store>", "bytes_per_launch": nbytes,
-                     "kernel_us": round(r["kernel_ms"] * 1e3, 2)},
+                     "avg_launch_us": round(r["kernel_ms"] * 1e3, 2),
+                     "timing": f"HIP events on the launch stream around {args.steps} back-to-back calls after "
+                               f"{args.warmup} untimed ones; each call is one launch of this kernel and nothing "
+                               f"else, so the region's length / {args.steps} is the kernel's average launch "
+                               f"duration (gaps between the queued launches included)"},
     }
+    out["fp8_pair"] = bench_fp8_pair(synth.workloads()["fp8long"], args.steps, args.warmup)
     if args.extra:
         extra = {"note": "us_per_call: average over back-to-back calls of the timed region (a call may launch "
                           "a clear and a total kernel around the main one)"}

@@ -338,6 +338,43 @@ def qk_tokens(spec: Spec, qkv_rows: np.ndarray, tokens, in_dt: str, w_q, w_k, q_
     return q, k, v, y
 
 
+def qk_tokens_store(spec: Spec, qkv_rows: np.ndarray, tokens, in_dt: str, w_q, w_k, q_dt="f32", k_dt="f16",
+                    threads: int = 1):
+    """The non-FP8 outputs (q, k, v [n_tok, H, D]) of selected tokens, the token list split into
+    `threads` contiguous blocks that run h3ref_qk_tokens_ex at the same time on host threads (ctypes
+    releases the interpreter lock during the call, and the oracle's row buffers are per thread).
+    Rows are independent, so the result does not depend on `threads`.  Used to time the oracle on
+    one core and on all cores; y' is not written out."""
+    from concurrent.futures import ThreadPoolExecutor
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    n = tokens.size
+    rows = np.ascontiguousarray(qkv_rows, dtype=np.uint16).reshape(n, spec.row_stride)
+    wq, wk = _f32(w_q), _f32(w_k)
+    ds = np.ones(3, np.float32)
+    shape = (n, spec.H, spec.D)
+    q = np.empty(shape, NP_DT[q_dt]); k = np.empty(shape, NP_DT[k_dt]); v = np.empty(shape, np.uint16)
+    P = spec.c()
+    L = lib()
+    cuts = [n * j // threads for j in range(threads + 1)]
+
+    def block(j):
+        a, b = cuts[j], cuts[j + 1]
+        if b <= a:
+            return 0
+        return L.h3ref_qk_tokens_ex(ctypes.byref(P), _ptr(rows[a:b]), DT[in_dt], _ptr(wq), _ptr(wk),
+                                    _ptr(tokens[a:b]), b - a, 0, _ptr(ds), 0, _ptr(q[a:b]), DT[q_dt], _ptr(k[a:b]),
+                                    DT[k_dt], _ptr(v[a:b]), None, None)
+
+    if threads == 1:
+        rcs = [block(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            rcs = list(ex.map(block, range(threads)))
+    if any(rcs):
+        raise ValueError(f"oracle: position outside the tables (rc={rcs})")
+    return q, k, v
+
+
 def norm_rope_row(x, w, eps, n, crow, srow):
     """One row through the oracle's norm + rotation; crow/srow: three length-n arrays (t, h, w)."""
     x, w = _f32(x), _f32(w)

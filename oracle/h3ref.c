@@ -24,6 +24,9 @@
  * function here is pinned by the tests (closed forms, brute force, library routines, the numpy
  * twin in twin.py).
  *
+ * Entry points keep their per-call row buffers in thread-local storage, so several host threads may
+ * call them at once on disjoint outputs (the bench times the oracle on one core and on all cores).
+ *
  * Arithmetic: IEEE binary32, one rounding per written operation, in the order written.
  * Build with -O2 -ffp-contract=off and without fast-math: no fused multiply-add, no
  * reassociation, no flush-to-zero.  sqrtf and '/' are correctly rounded on x86-64 SSE.
@@ -293,7 +296,7 @@ static int run_items(const h3ref_problem *P, const void *qkv, int in_dt, const f
                      void *v) {
     int H = P->H, D = P->D;
     int64_t plane = (int64_t)H * P->T * D;
-    static float yqk[2 * 64 * 256];
+    static __thread float yqk[2 * 64 * 256];
     if (H > 64 || D > 256) return -2;
     for (int b = 0; b < P->B; ++b)
         for (int64_t i = 0; i < P->T; ++i) {
@@ -323,7 +326,7 @@ int h3ref_qk_rmsnorm_rope_permute(const h3ref_problem *P, const void *qkv, int i
  */
 int h3ref_qk_amax(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q,
                   const float *w_k, float amax[2]) {
-    static float yqk[2 * 64 * 256];
+    static __thread float yqk[2 * 64 * 256];
     int H = P->H, D = P->D;
     if (H > 64 || D > 256) return -2;
     amax[0] = 0.0f; amax[1] = 0.0f;
@@ -384,7 +387,7 @@ int h3ref_qk_tokens_ex(const h3ref_problem *P, const void *qkv_rows, int in_dt, 
                        const float *w_k, const int64_t *tokens, int64_t n_tok, int fp8,
                        const float *descale, int v_fp8, void *q, int q_dt, void *k, int k_dt, void *v,
                        float *yf32, uint64_t *sat) {
-    static float yqk[2 * 64 * 256];
+    static __thread float yqk[2 * 64 * 256];
     int H = P->H, D = P->D;
     if (H > 64 || D > 256) return -2;
     store_opts so = {fp8 ? 1 : 0, fp8 && v_fp8 ? 1 : 0, {1.0f, 1.0f, 1.0f}, sat};
@@ -491,7 +494,7 @@ static int token_tensor(const h3ref_problem *P, const uint16_t *row, int in_dt, 
 /* 16-bit or f32 output: out = RN_out_dt(y'), +0 for padded tokens. */
 int h3ref_tensor_norm_rope(const h3ref_problem *P, const void *x, int in_dt, const float *w, void *out,
                            int out_dt, int layout) {
-    static float y[64 * 256];
+    static __thread float y[64 * 256];
     if (P->H > 64 || P->D > 256) return -2;
     for (int b = 0; b < P->B; ++b)
         for (int64_t i = 0; i < P->T; ++i) {
@@ -510,7 +513,7 @@ int h3ref_tensor_norm_rope(const h3ref_problem *P, const void *x, int in_dt, con
 
 /* amax = max |y'| over the valid rows (NaN propagates; +0 when nothing is valid). */
 int h3ref_tensor_amax(const h3ref_problem *P, const void *x, int in_dt, const float *w, float *amax) {
-    static float y[64 * 256];
+    static __thread float y[64 * 256];
     if (P->H > 64 || P->D > 256) return -2;
     *amax = 0.0f;
     for (int b = 0; b < P->B; ++b)
@@ -532,7 +535,7 @@ int h3ref_tensor_amax(const h3ref_problem *P, const void *x, int in_dt, const fl
    overwritten with the count of valid elements whose quotient exceeds 448 in magnitude. */
 int h3ref_tensor_cast_e4m3(const h3ref_problem *P, const void *x, int in_dt, const float *w, float scale,
                            int is_descale, uint8_t *out, int layout, float *descale, uint64_t *sat) {
-    static float y[64 * 256];
+    static __thread float y[64 * 256];
     if (P->H > 64 || P->D > 256) return -2;
     float ds = is_descale ? h3ref_static_descale(scale) : h3ref_descale(scale);
     if (descale) *descale = ds;
@@ -560,7 +563,7 @@ int h3ref_tensor_cast_e4m3(const h3ref_problem *P, const void *x, int in_dt, con
  */
 int h3ref_qk_sage(const h3ref_problem *P, const void *qkv, int in_dt, const float *w_q, const float *w_k,
                   float kv_scale, float *q, float *k, uint16_t *v) {
-    static float yqk[2 * 64 * 256];
+    static __thread float yqk[2 * 64 * 256];
     int H = P->H, D = P->D;
     if (H > 64 || D > 256) return -2;
     int64_t plane = (int64_t)H * P->T * D;

@@ -17,8 +17,8 @@ SOURCES = [os.path.join(CSRC, f) for f in ("h3qk_kernels.hip", "h3_tensor_kernel
 HEADERS = [os.path.join(ROOT, "include", "h3qk.h"), os.path.join(CSRC, "h3qk_internal.h"),
            os.path.join(CSRC, "h3qk_device.h")]
 # test-only check kernels over the library's device helpers, built beside their sources
-CHECK_SRC = os.path.join(ROOT, "tests", "hip", "rsqrt_check.hip")
-CHECK_LIB = os.path.join(ROOT, "tests", "hip", "librsqrt_check.so")
+CHECK_SRC = os.path.join(ROOT, "tests", "hip", "h3check.hip")
+CHECK_LIB = os.path.join(ROOT, "tests", "hip", "libh3check.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

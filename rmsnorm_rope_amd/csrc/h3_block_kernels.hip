@@ -92,10 +92,12 @@ __global__ __launch_bounds__(256) void scaled_residual_kernel(const float *__res
   }
 }
 
+// vectors < 2^32 (the host's limit): at most 2^23 blocks, and the kernels' 32-bit vector index
+// blockIdx.x * 512 + 256 v + threadIdx.x stays below 2^32.
 int launch(const void *kern, uint32_t vectors, void **args, hipStream_t stream, std::string *err) {
-    const uint32_t blocks = (vectors + 256u * kVectorsPerThread - 1u) / (256u * kVectorsPerThread);
+    const uint64_t blocks = blocks_for(vectors, 256u * kVectorsPerThread);
     if (blocks == 0) return H3_OK;
-    const hipError_t e = hipLaunchKernel(kern, dim3(blocks), dim3(256), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, 0, stream);
     if (e != hipSuccess) {
         *err = std::string("kernel launch failed: ") + hipGetErrorString(e);
         return H3_ELAUNCH;

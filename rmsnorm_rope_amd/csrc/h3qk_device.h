@@ -411,6 +411,11 @@ __device__ __forceinline__ float quotient(float y, float ds, float rcp) {
     return __builtin_fmaf(-e1, rcp, q1);
 }
 
+// A non-NaN quotient brought into the E4M3 range [-448, 448] (v_med3; +-inf included) ahead of the
+// conversion instruction: the encoder saturates everything past 448 to +-448, so the code of the
+// clamped value is the code of the value.
+__device__ __forceinline__ float clamp_e4m3(float q) { return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f); }
+
 // Codes of W quotients as W/4 packed words.  hw: the conversion instruction, exact for |q| <= 448
 // (the caller guarantees that range); otherwise the integer encoder (saturation, NaN).
 template <int W>
@@ -496,7 +501,7 @@ __device__ __forceinline__ void cast_e4m3_wave(const float (&y)[M][W], float ds,
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int k = 0; k < W; ++k) q[m][k] = __builtin_amdgcn_fmed3f(q[m][k], -448.0f, 448.0f);
+            for (int k = 0; k < W; ++k) q[m][k] = clamp_e4m3(q[m][k]);
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) pack_e4m3<W>(q[m], !exact, w[m]);

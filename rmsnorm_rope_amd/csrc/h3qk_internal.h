@@ -43,6 +43,12 @@ H3_HD inline uint32_t div_apply(uint32_t n, const DivMagic &g) {
     return (t + ((n - t) >> g.s1)) >> g.s2;
 }
 
+// Blocks of a one-dimensional launch covering `units` work units, `per_block` per block, counted in
+// 64 bits: the elementwise ops accept up to 2^32 - 1 units, where a 32-bit sum would wrap to zero.
+H3_HD constexpr uint64_t blocks_for(uint64_t units, uint64_t per_block) {
+    return (units + per_block - 1) / per_block;
+}
+
 #ifndef H3QK_NO_HIP
 enum Mode : int { MODE_STORE = 0, MODE_AMAX = 1, MODE_CAST = 2 };
 

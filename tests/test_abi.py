@@ -319,3 +319,44 @@ def test_block_op_validation():
     with pytest.raises(h3.H3Error) as e:
         h3.h3_scaled_residual(R, Bq + 4, h3.F16, S, 8, O, 4, 8, stream=0)
     assert e.value.name == "H3_EALIGN"
+
+
+def test_elementwise_launch_covers_the_largest_accepted_size(tmp_path):
+    """The decoder-block ops accept up to 2^32 - 1 vectors (N * F / 8 for SwiGLU, N * C / 4 for the
+    scaled residual).  Their block count is taken in 64 bits (a 32-bit sum would wrap to zero blocks
+    at the top of that range and the call would return success having written nothing), and the
+    multiply-high division that maps a vector to its row is exact there.  Host code of the library's
+    internal header, compiled with g++ (no GPU)."""
+    src = tmp_path / "blocks.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include "h3qk_internal.h"
+int main() {
+    int bad = 0;
+    const uint64_t top = 0xFFFFFFFFull;  // the largest vector count the host accepts
+    const uint64_t per = 512;            // vectors per block of the elementwise kernels
+    const uint64_t vs[] = {1, 511, 512, 513, top - 512, top - 511, top - 1, top};
+    for (uint64_t v : vs) {
+        const uint64_t b = h3::blocks_for(v, per);
+        if (b == 0 || b * per < v || (b - 1) * per >= v) { std::printf("blocks %llu\n", (unsigned long long)v); ++bad; }
+        if (b > (1ull << 23)) { std::printf("more than 2^23 blocks at %llu\n", (unsigned long long)v); ++bad; }
+    }
+    const uint32_t ds[] = {1u, 2u, 3u, 7u, 256u, 1000u, 1024u, 4095u, 1u << 27};
+    for (uint32_t d : ds) {
+        const h3::DivMagic m = h3::div_magic(d);
+        const uint64_t ns[] = {0, 1, (uint64_t)d - 1, (uint64_t)d, 0x7FFFFFFF, top - d, top - 1, top};
+        for (uint64_t n : ns) {
+            if (n > top) continue;
+            if (h3::div_apply((uint32_t)n, m) != (uint32_t)n / d) { std::printf("div %llu / %u\n", (unsigned long long)n, d); ++bad; }
+        }
+    }
+    std::printf("%d failure(s)\n", bad);
+    return bad != 0;
+}
+''')
+    exe = tmp_path / "blocks"
+    r = subprocess.run(["g++", "-std=c++17", "-O1", "-DH3QK_NO_HIP", "-I", os.path.join(ROOT, "rmsnorm_rope_amd", "csrc"),
+                        "-o", str(exe), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and "0 failure(s)" in out.stdout, out.stdout + out.stderr

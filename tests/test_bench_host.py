@@ -72,3 +72,25 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_oracle_on_all_cores_matches_one_thread():
+    """The CPU baseline's driver: the oracle's token entry on disjoint blocks run by 8 host threads
+    at once gives the bits of one thread and of the whole-problem entry (head-major there)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth.problem import oracle_spec
+    wl = synth.workloads()["tile"]
+    sp = oracle_spec(wl)
+    x = synth.qkv_host(wl)
+    wq, wk = synth.norm_weights(wl)
+    toks = np.arange(wl.T)
+    one = oracle.qk_tokens_store(sp, x[0], toks, "f16", wq, wk, threads=1)
+    many = oracle.qk_tokens_store(sp, x[0], toks, "f16", wq, wk, threads=8)
+    for a, b in zip(one, many):
+        assert np.array_equal(a, b)
+    q, k, v = oracle.qk_rmsnorm_rope_permute(sp, x, "f16", wq, wk, "f32", "f16")
+    for whole, tok in zip((q, k, v), many):
+        assert np.array_equal(whole[0].transpose(1, 0, 2), tok)

@@ -2,7 +2,7 @@
 hardware square root corrected by two FMA residuals, then the hardware reciprocal with one FMA
 Newton step) gives the bits of 1.0f / sqrtf(v), both correctly rounded, for every binary32 v in
 [2^-96, +inf] and for every NaN pattern: an exhaustive check on the GPU through the library's
-own device code (tests/hip/rsqrt_check.hip)."""
+own device code (tests/hip/h3check.hip)."""
 import ctypes
 import os
 import struct
