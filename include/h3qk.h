@@ -40,7 +40,8 @@
  *     itself is a HOST struct read during the call only;
  *   - work is enqueued on `stream` (0 = the null stream) and is asynchronous: no host sync;
  *   - the caller owns every buffer; the library allocates no device or host memory and keeps no
- *     pointer after it returns;
+ *     pointer after it returns (h3_qk_cast_e4m3_static_noalloc's scratch is a static array of
+ *     the library's device code, not an allocation);
  *   - arguments are validated on the host before anything is enqueued: a call that returns an
  *     error has enqueued nothing (all or nothing), and h3_last_error() describes the failure;
  *   - the unsupported cases return H3_EUNSUPPORTED so a caller can keep its own path;
@@ -172,15 +173,35 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
  *   sat_qkv      DEVICE uint64 [H3_SAT_WORDS], or NULL: a clip-counter buffer, overwritten.
  *                sat_qkv[0..2] receive the number of valid elements of Q, K, V whose binary32
  *                quotient exceeds 448 in magnitude (saturated codes; a NaN quotient is not counted;
- *                sat_qkv[2] = 0 when V is copied).  The rest of the buffer holds per-slot partial
- *                counts (it is cleared, added to, then summed, all on the stream).  8-byte aligned,
- *                not overlapping any other argument.
+ *                sat_qkv[2] = 0 when V is copied).  Words 16 on hold H3_SAT_SLOTS per-slot partial
+ *                counts (cleared, added to, then summed, all on the stream); words 3..15 are not
+ *                used.  8-byte aligned, not overlapping any other argument.
  * With descale_s = amax_s / 448 this writes the codes h3_qk_cast_e4m3 writes.
  */
 int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
                            const float *w_q, const float *w_k, const float *descale_qkv,
                            uint8_t *q_codes, uint8_t *k_codes, void *v_out, h3_dtype v_dt,
                            uint64_t *sat_qkv, hipStream_t stream);
+
+/*
+ * h3_qk_cast_e4m3_static for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and outputs,
+ * except that no counter buffer is passed in:
+ *   sat_counts   DEVICE uint64 [3], or NULL: receives the three clip counts (Q, K, V) that
+ *                h3_qk_cast_e4m3_static writes to sat_qkv[0..2].  8-byte aligned.
+ * The partial counts live in a static device array of the library, H3_SAT_SLOTS slots of 128
+ * bytes (16 KiB), one copy per GPU held until the process ends, cleared by a kernel at the start
+ * of each call.  Its size does not depend on the problem (a block adds into slot blockIdx mod
+ * H3_SAT_SLOTS), so every problem h3_qk_cast_e4m3_static accepts fits it and the size limits are
+ * those of that call.  Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race on it and their counts may be wrong; their
+ * codes are not affected.  No hipMalloc, hipFree or other allocation is made (the array's device
+ * address is looked up once per GPU, on the first call there).
+ */
+int h3_qk_cast_e4m3_static_noalloc(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
+                                   const float *w_q, const float *w_k, const float *descale_qkv,
+                                   uint8_t *q_codes, uint8_t *k_codes, void *v_out, h3_dtype v_dt,
+                                   uint64_t *sat_counts, hipStream_t stream);
 
 /*
  * FP8 recipe with V cast too ([TRT-21485]: Q, K and V cast to E4M3 with per-tensor scales, a

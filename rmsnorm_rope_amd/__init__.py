@@ -14,6 +14,7 @@ from typing import Optional, Sequence
 __all__ = [
     "F32", "F16", "BF16", "E4M3FN", "MAX_BATCH", "SAT_WORDS", "H3Error", "QkDesc", "make_desc", "lib",
     "h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_qk_cast_e4m3_static",
+    "h3_qk_cast_e4m3_static_noalloc",
     "h3_qk_rmsnorm_rope_permute_sage", "h3_qkv_amax", "h3_qkv_cast_e4m3", "h3_tensor_norm_rope", "h3_tensor_amax", "h3_tensor_cast_e4m3",
     "LAYOUT_BHTD", "LAYOUT_BTHD", "h3_swiglu", "h3_scaled_residual",
     "h3_last_error", "h3_abi_version",
@@ -33,6 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh3qk.so"
 
 # every function include/h3qk.h declares
 EXPORTS = ("h3_qk_rmsnorm_rope_permute", "h3_qk_amax", "h3_qk_cast_e4m3", "h3_qk_cast_e4m3_static",
+           "h3_qk_cast_e4m3_static_noalloc",
            "h3_qk_rmsnorm_rope_permute_sage", "h3_qkv_amax", "h3_qkv_cast_e4m3", "h3_tensor_norm_rope",
            "h3_tensor_amax", "h3_tensor_cast_e4m3", "h3_swiglu", "h3_scaled_residual", "h3_last_error", "h3_abi_version")
 
@@ -73,6 +75,7 @@ def lib():
         L.h3_qk_amax.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.h3_qk_cast_e4m3.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.h3_qk_cast_e4m3_static.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        L.h3_qk_cast_e4m3_static_noalloc.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         L.h3_qk_rmsnorm_rope_permute_sage.argtypes = [D, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         L.h3_qkv_amax.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.h3_qkv_cast_e4m3.argtypes = [D, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -186,6 +189,14 @@ def h3_qk_cast_e4m3_static(desc: QkDesc, qkv, in_dt, w_q, w_k, descale_qkv, q_co
                                       _ptr(descale_qkv), _ptr(q_codes), _ptr(k_codes), _ptr(v_out), _dt(v_dt),
                                       _ptr(sat_qkv), _stream(stream))
     _check("h3_qk_cast_e4m3_static", rc)
+
+
+def h3_qk_cast_e4m3_static_noalloc(desc: QkDesc, qkv, in_dt, w_q, w_k, descale_qkv, q_codes, k_codes, v_out,
+                                   v_dt, sat_counts=None, stream=None) -> None:
+    rc = lib().h3_qk_cast_e4m3_static_noalloc(ctypes.byref(desc), _ptr(qkv), _dt(in_dt), _ptr(w_q), _ptr(w_k),
+                                              _ptr(descale_qkv), _ptr(q_codes), _ptr(k_codes), _ptr(v_out),
+                                              _dt(v_dt), _ptr(sat_counts), _stream(stream))
+    _check("h3_qk_cast_e4m3_static_noalloc", rc)
 
 
 def h3_qk_rmsnorm_rope_permute_sage(desc: QkDesc, qkv, in_dt, w_q, w_k, kv_scale: float, q_out, k_out, v_out,

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
         const int64_t o = obase + u * p.out_hstride;
         if constexpr (MODE == MODE_CAST) {
             uint32_t cw[M][W / 4];
-            cast_e4m3_wave<M, W>(x[u], ds, rcp, fast, p.sat != nullptr, nsat, cw);
+            cast_e4m3_wave<M, W>(x[u], ds, rcp, fast, p.sat_slots != nullptr, nsat, cw);
             if constexpr (W == 8 && M == 2) {
                 store_words_pairs<1, W>(p.q, o + olane, c, cw[0], cw[1]);
             } else {
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
     }
     if constexpr (MODE == MODE_CAST) {
         if (nsat && lane == (int)__builtin_ctzll(__builtin_amdgcn_read_exec()))
-            atomicAdd(p.sat + 16 * (1 + (blockIdx.x & (H3_SAT_SLOTS - 1))), (unsigned long long)nsat);
+            atomicAdd(p.sat_slots + 16 * (blockIdx.x & (H3_SAT_SLOTS - 1)), (unsigned long long)nsat);
     }
 }
 
@@ -275,14 +275,14 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
         return launch_kernel(reinterpret_cast<const void *>(kern), blocks, 0, p, stream, err);
     } else {
         auto kern = tensor_kernel<D, IN, OT, MODE, NN, NORM>;
-        if (MODE == MODE_CAST && p.sat) {
-            const int rc = clear_words(reinterpret_cast<uint32_t *>(p.sat), 2 * H3_SAT_WORDS, stream, "clip counter", err);
+        if (MODE == MODE_CAST && p.sat_slots) {
+            const int rc = clear_sat_slots(p.sat_slots, stream, err);
             if (rc != H3_OK) return rc;
         }
         const size_t lds = (size_t)(f.lds_per_cu / kTensorBlocksPerCU);
         const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + 3) / 4, lds, p, stream, err);
-        if (rc != H3_OK || MODE != MODE_CAST || !p.sat) return rc;
-        return sat_total(p.sat, stream, err);
+        if (rc != H3_OK || MODE != MODE_CAST || !p.sat_slots) return rc;
+        return sat_total(p.sat_slots, p.sat, stream, err);
     }
 }
 

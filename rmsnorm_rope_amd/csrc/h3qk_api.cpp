@@ -4,8 +4,8 @@
 #include <string.h>
 
 #include <cmath>
+#include <initializer_list>
 #include <string>
-#include <vector>
 
 #include "h3qk.h"
 #include "h3qk_internal.h"
@@ -24,6 +24,28 @@ struct Range {
     const char *name;
 };
 
+// The address ranges of one call's inputs or outputs, held in place: validation of a call that
+// succeeds allocates no memory.  A call has at most 6 inputs and 5 outputs.
+class RangeList {
+  public:
+    RangeList() = default;
+    RangeList(std::initializer_list<Range> l) {
+        for (const Range &r : l) push_back(r);
+    }
+    void push_back(const Range &r) {
+        if (n_ < kCap) r_[n_++] = r;
+    }
+    size_t size() const { return (size_t)n_; }
+    const Range &operator[](size_t i) const { return r_[i]; }
+    const Range *begin() const { return r_; }
+    const Range *end() const { return r_ + n_; }
+
+  private:
+    static constexpr int kCap = 8;
+    Range r_[kCap];
+    int n_ = 0;
+};
+
 bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
 
 int elem_size(int dt) { return dt == H3_F32 ? 4 : (dt == H3_E4M3FN ? 1 : 2); }
@@ -34,7 +56,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Q | K | V row) and the one-tensor calls (tensors = 1: w_q is the tensor's weight, NULL for the
 // identity; w_k unused); fill the kernel parameters.  Returns H3_OK or an error code with g_err set.
 int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q, const float *w_k,
-               h3::QkParams *p, std::vector<Range> *inputs, int tensors = 3) {
+               h3::QkParams *p, RangeList *inputs, int tensors = 3) {
     if (!d) return fail(H3_EINVAL, "desc is NULL");
     if (tensors == 3 && (!qkv || !w_q || !w_k)) return fail(H3_EINVAL, "qkv, w_q and w_k must be non-NULL");
     if (tensors == 1 && !qkv) return fail(H3_EINVAL, "x must be non-NULL");
@@ -124,7 +146,7 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
     return H3_OK;
 }
 
-int check_outputs(const std::vector<Range> &inputs, const std::vector<Range> &outputs) {
+int check_outputs(const RangeList &inputs, const RangeList &outputs) {
     for (size_t i = 0; i < outputs.size(); ++i) {
         if (!aligned16(reinterpret_cast<const void *>(outputs[i].lo)))
             return fail(H3_EALIGN, std::string(outputs[i].name) + " must be 16-byte aligned");
@@ -159,7 +181,7 @@ int h3_qk_rmsnorm_rope_permute(const h3_qk_desc *desc, const void *qkv, h3_dtype
                                const float *w_q, const float *w_k, void *q_out, h3_dtype q_dt,
                                void *k_out, h3_dtype k_dt, void *v_out, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!q_out || !k_out || !v_out) return fail(H3_EINVAL, "q_out, k_out and v_out must be non-NULL");
@@ -181,7 +203,7 @@ int h3_qk_rmsnorm_rope_permute_sage(const h3_qk_desc *desc, const void *qkv, h3_
                                     const float *w_k, float kv_scale, float *q_out, float *k_out, uint16_t *v_out,
                                     hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!q_out || !k_out || !v_out) return fail(H3_EINVAL, "q_out, k_out and v_out must be non-NULL");
@@ -201,7 +223,7 @@ int h3_qk_rmsnorm_rope_permute_sage(const h3_qk_desc *desc, const void *qkv, h3_
 int h3_qk_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
                const float *w_k, float *amax_qk, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!amax_qk) return fail(H3_EINVAL, "amax_qk must be non-NULL");
@@ -217,7 +239,7 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, con
                     const float *w_k, const float *amax_qk, uint8_t *q_codes, uint8_t *k_codes,
                     void *v_out, float *descale_qk, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!amax_qk || !q_codes || !k_codes || !v_out || !descale_qk)
@@ -228,7 +250,7 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, con
     inputs.push_back({a, a + 8, "amax_qk"});
     const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
     const uintptr_t ds = reinterpret_cast<uintptr_t>(descale_qk);
-    std::vector<Range> outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
+    RangeList outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
                                out_range(v_out, n, in_dt, "v_out")};
     rc = check_outputs(inputs, outs);
     if (rc) return rc;
@@ -245,11 +267,19 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, con
     return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
 }
 
-int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
-                           const float *w_k, const float *descale_qkv, uint8_t *q_codes, uint8_t *k_codes,
-                           void *v_out, h3_dtype v_dt, uint64_t *sat_qkv, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The static-scale cast with the clip counts written to `sat` (sat_words words, the counts in the
+// first three) and the partial counts kept in `slots` (H3_SAT_SLOTS slots of 16 words): the
+// caller's counter buffer for both (slots from its word 16 on), or the caller's three words and
+// the library's static scratch.  sat == NULL: no counting.
+int cast_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q, const float *w_k,
+                const float *descale_qkv, uint8_t *q_codes, uint8_t *k_codes, void *v_out, h3_dtype v_dt,
+                uint64_t *sat, int sat_words, const char *sat_name, bool own_slots, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!descale_qkv || !q_codes || !k_codes || !v_out)
@@ -257,36 +287,60 @@ int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_
     if (v_dt != in_dt && v_dt != H3_E4M3FN) return fail(H3_EUNSUPPORTED, "v_dt must be in_dt or H3_E4M3FN");
     const bool v_fp8 = v_dt == H3_E4M3FN;
     if (reinterpret_cast<uintptr_t>(descale_qkv) & 3u) return fail(H3_EALIGN, "descale_qkv must be 4-byte aligned");
-    if (reinterpret_cast<uintptr_t>(sat_qkv) & 7u) return fail(H3_EALIGN, "sat_qkv must be 8-byte aligned");
+    if (reinterpret_cast<uintptr_t>(sat) & 7u) return fail(H3_EALIGN, std::string(sat_name) + " must be 8-byte aligned");
     const uintptr_t a = reinterpret_cast<uintptr_t>(descale_qkv);
     inputs.push_back({a, a + (v_fp8 ? 12u : 8u), "descale_qkv"});
     const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
-    std::vector<Range> outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
-                               out_range(v_out, n, v_dt, "v_out")};
+    RangeList outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
+                      out_range(v_out, n, v_dt, "v_out")};
     rc = check_outputs(inputs, outs);
     if (rc) return rc;
-    if (sat_qkv) {
-        const uintptr_t sp = reinterpret_cast<uintptr_t>(sat_qkv);
-        const Range sr = {sp, sp + (uintptr_t)H3_SAT_WORDS * 8, "sat_qkv"};
+    if (sat) {
+        const uintptr_t sp = reinterpret_cast<uintptr_t>(sat);
+        const Range sr = {sp, sp + (uintptr_t)sat_words * 8, sat_name};
         for (const Range &r : inputs)
-            if (overlaps(sr, r)) return fail(H3_EALIAS, std::string("sat_qkv overlaps input ") + r.name);
+            if (overlaps(sr, r)) return fail(H3_EALIAS, std::string(sat_name) + " overlaps input " + r.name);
         for (const Range &r : outs)
-            if (overlaps(sr, r)) return fail(H3_EALIAS, std::string("sat_qkv overlaps output ") + r.name);
+            if (overlaps(sr, r)) return fail(H3_EALIAS, std::string(sat_name) + " overlaps output " + r.name);
+        p.sat = reinterpret_cast<unsigned long long *>(sat);
+        if (own_slots) {
+            p.sat_slots = p.sat + 16;
+        } else {
+            std::string err;
+            if (!h3::scratch_slots(&p.sat_slots, &err)) return fail(H3_ELAUNCH, err);
+        }
     }
     p.amax = const_cast<float *>(descale_qkv);
     p.static_scale = 1;
     p.v_fp8 = v_fp8 ? 1 : 0;
-    p.sat = reinterpret_cast<unsigned long long *>(sat_qkv);
     p.q = q_codes;
     p.k = k_codes;
     p.v = v_out;
     return run(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, H3_E4M3FN, p, stream);
 }
 
+}  // namespace
+
+extern "C" {
+
+int h3_qk_cast_e4m3_static(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                           const float *w_k, const float *descale_qkv, uint8_t *q_codes, uint8_t *k_codes,
+                           void *v_out, h3_dtype v_dt, uint64_t *sat_qkv, hipStream_t stream) {
+    return cast_static(desc, qkv, in_dt, w_q, w_k, descale_qkv, q_codes, k_codes, v_out, v_dt, sat_qkv, H3_SAT_WORDS,
+                       "sat_qkv", true, stream);
+}
+
+int h3_qk_cast_e4m3_static_noalloc(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
+                                   const float *w_k, const float *descale_qkv, uint8_t *q_codes, uint8_t *k_codes,
+                                   void *v_out, h3_dtype v_dt, uint64_t *sat_counts, hipStream_t stream) {
+    return cast_static(desc, qkv, in_dt, w_q, w_k, descale_qkv, q_codes, k_codes, v_out, v_dt, sat_counts, 3,
+                       "sat_counts", false, stream);
+}
+
 int h3_qkv_amax(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, const float *w_q,
                 const float *w_k, float *amax_qkv, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!amax_qkv) return fail(H3_EINVAL, "amax_qkv must be non-NULL");
@@ -303,7 +357,7 @@ int h3_qkv_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, co
                      const float *w_k, const float *amax_qkv, uint8_t *q_codes, uint8_t *k_codes,
                      uint8_t *v_codes, float *descale_qkv, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, qkv, in_dt, w_q, w_k, &p, &inputs);
     if (rc) return rc;
     if (!amax_qkv || !q_codes || !k_codes || !v_codes || !descale_qkv)
@@ -313,7 +367,7 @@ int h3_qkv_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt, co
     const uintptr_t a = reinterpret_cast<uintptr_t>(amax_qkv);
     inputs.push_back({a, a + 12, "amax_qkv"});
     const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
-    std::vector<Range> outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
+    RangeList outs = {out_range(q_codes, n, H3_E4M3FN, "q_codes"), out_range(k_codes, n, H3_E4M3FN, "k_codes"),
                                out_range(v_codes, n, H3_E4M3FN, "v_codes")};
     rc = check_outputs(inputs, outs);
     if (rc) return rc;
@@ -361,7 +415,7 @@ int run_tensor(int mode, int D, int in_dt, int out_dt, bool norm, h3::QkParams &
 int h3_tensor_norm_rope(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w, void *out,
                         h3_dtype out_dt, h3_layout out_layout, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, x, in_dt, w, nullptr, &p, &inputs, 1);
     if (rc) return rc;
     if (!out) return fail(H3_EINVAL, "out must be non-NULL");
@@ -380,7 +434,7 @@ int h3_tensor_norm_rope(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
 int h3_tensor_amax(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, const float *w, float *amax,
                    hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, x, in_dt, w, nullptr, &p, &inputs, 1);
     if (rc) return rc;
     if (!amax) return fail(H3_EINVAL, "amax must be non-NULL");
@@ -397,7 +451,7 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
                         const float *scale, int scale_is_descale, uint8_t *codes, h3_layout out_layout,
                         float *descale, uint64_t *sat, hipStream_t stream) {
     h3::QkParams p;
-    std::vector<Range> inputs;
+    RangeList inputs;
     int rc = check_desc(desc, x, in_dt, w, nullptr, &p, &inputs, 1);
     if (rc) return rc;
     if (!scale || !codes) return fail(H3_EINVAL, "scale and codes must be non-NULL");
@@ -410,7 +464,7 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
     const uintptr_t a = reinterpret_cast<uintptr_t>(scale);
     inputs.push_back({a, a + 4, "scale"});
     const int64_t n = (int64_t)desc->B * desc->H * desc->T * desc->D;
-    std::vector<Range> outs = {out_range(codes, n, H3_E4M3FN, "codes")};
+    RangeList outs = {out_range(codes, n, H3_E4M3FN, "codes")};
     rc = check_outputs(inputs, outs);
     if (rc) return rc;
     if (descale) {
@@ -433,6 +487,7 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
     p.static_scale = scale_is_descale;
     p.descale = descale;
     p.sat = reinterpret_cast<unsigned long long *>(sat);
+    p.sat_slots = sat ? p.sat + 16 : nullptr;
     p.q = codes;
     return run_tensor(h3::MODE_CAST, desc->D, in_dt, H3_E4M3FN, w != nullptr, p, stream);
 }

@@ -79,7 +79,9 @@ struct QkParams {
     float *amax;        // MODE_AMAX: reduced into (cleared first); MODE_CAST: read (amaxes, or
                         // descales when static_scale)
     float *descale;     // MODE_CAST: written by the first wave, or null
-    unsigned long long *sat;  // MODE_CAST: per-tensor counts of |quotient| > 448 (cleared first), or null
+    unsigned long long *sat;  // MODE_CAST: the per-tensor counts of |quotient| > 448 (3 words), or null
+    unsigned long long *sat_slots;  // MODE_CAST with sat: H3_SAT_SLOTS slots of 16 words (one 128-byte
+                                    // line each) where waves add partial counts; cleared first
     int64_t row_stride;
     int64_t batch_stride;
     int64_t items;               // B * groups * head_chunks
@@ -122,8 +124,15 @@ int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hip
 // Zero n words on the stream (one block).
 int clear_words(uint32_t *a, int n, hipStream_t stream, const char *what, std::string *err);
 
+// Zero the H3_SAT_SLOTS partial-count slots (one block, on the stream).
+int clear_sat_slots(unsigned long long *slots, hipStream_t stream, std::string *err);
+
 // sat[0..2] = sums of the clip-counter slots (one wave, on the stream).
-int sat_total(unsigned long long *sat, hipStream_t stream, std::string *err);
+int sat_total(const unsigned long long *slots, unsigned long long *sat, hipStream_t stream, std::string *err);
+
+// Device address of this GPU's copy of the library's static partial-count slots (the scratch of
+// the allocation-free static cast), looked up on the first call on each device and kept.
+bool scratch_slots(unsigned long long **slots, std::string *err);
 
 // Launch one QK pass.  Returns H3_OK or H3_ELAUNCH / H3_EUNSUPPORTED with *err filled.
 int launch_qk(int mode, int D, int in_dt, int q_dt, int k_dt, QkParams &p, hipStream_t stream,

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
                     xv[vc][e] = in_to_f32<IN>((e & 1) ? (wd >> 16) : (wd & 0xFFFFu));
                 }
             uint32_t cv[VC][2];
-            cast_e4m3_wave<VC, 8>(xv, ds[2], rcp[2], fast, p.sat != nullptr, nsat[2], cv);
+            cast_e4m3_wave<VC, 8>(xv, ds[2], rcp[2], fast, p.sat_slots != nullptr, nsat[2], cv);
             if constexpr (VC == 2) {  // each token's 128-byte row in one instruction
                 store_words_pairs<1, 8>(p.v, o + olane, c, cv[0], cv[1]);
             } else {  // 8 tokens' 64-byte rows: 512 contiguous bytes
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
         row_scale_rotate<W, M>(xk, rr[2 * u + 1], wk, cs, sn, rot);
         if constexpr (MODE == MODE_CAST) {
             uint32_t cw[2][M][W / 4];
-            cast_e4m3_wave<M, W>(xq, ds[0], rcp[0], fast, p.sat != nullptr, nsat[0], cw[0]);
-            cast_e4m3_wave<M, W>(xk, ds[1], rcp[1], fast, p.sat != nullptr, nsat[1], cw[1]);
+            cast_e4m3_wave<M, W>(xq, ds[0], rcp[0], fast, p.sat_slots != nullptr, nsat[0], cw[0]);
+            cast_e4m3_wave<M, W>(xk, ds[1], rcp[1], fast, p.sat_slots != nullptr, nsat[1], cw[1]);
             if constexpr (W == 8 && M == 2) {
                 store_words_pairs<1, W>(p.q, o + olane, c, cw[0][0], cw[0][1]);
                 store_words_pairs<1, W>(p.k, o + olane, c, cw[1][0], cw[1][1]);
@@ -272,8 +272,8 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
     }
     if constexpr (MODE == MODE_CAST) {
         // partial counts spread over slots (one 128-byte line each) to keep the atomics apart
-        if (p.sat && (nsat[0] | nsat[1] | nsat[2]) && lane == (int)__builtin_ctzll(__builtin_amdgcn_read_exec())) {
-            unsigned long long *slot = p.sat + 16 * (1 + (blockIdx.x & (H3_SAT_SLOTS - 1)));
+        if (p.sat_slots && (nsat[0] | nsat[1] | nsat[2]) && lane == (int)__builtin_ctzll(__builtin_amdgcn_read_exec())) {
+            unsigned long long *slot = p.sat_slots + 16 * (blockIdx.x & (H3_SAT_SLOTS - 1));
             if (nsat[0]) atomicAdd(slot, (unsigned long long)nsat[0]);
             if (nsat[1]) atomicAdd(slot + 1, (unsigned long long)nsat[1]);
             if (nsat[2]) atomicAdd(slot + 2, (unsigned long long)nsat[2]);
@@ -435,13 +435,13 @@ int clear_words(uint32_t *a, int n, hipStream_t stream, const char *what, std::s
 
 namespace {
 
-// Totals of the clip-counter slots: sat[t] = sum over slots of sat[16 (1 + slot) + t], one wave.
-__global__ __launch_bounds__(64) void sat_total_kernel(unsigned long long *sat) {
+// Totals of the clip-counter slots: sat[t] = sum over slots of slots[16 slot + t], one wave.
+__global__ __launch_bounds__(64) void sat_total_kernel(const unsigned long long *slots, unsigned long long *sat) {
     const int l = threadIdx.x;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
         unsigned long long v = 0;
-        for (int s = l; s < H3_SAT_SLOTS; s += 64) v += sat[16 * (1 + s) + t];
+        for (int s = l; s < H3_SAT_SLOTS; s += 64) v += slots[16 * s + t];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
         if (l == 0) sat[t] = v;
@@ -450,14 +450,46 @@ __global__ __launch_bounds__(64) void sat_total_kernel(unsigned long long *sat) 
 
 }  // namespace
 
-int sat_total(unsigned long long *sat, hipStream_t stream, std::string *err) {
-    hipLaunchKernelGGL(sat_total_kernel, dim3(1), dim3(64), 0, stream, sat);
+// Partial clip counts of the allocation-free static cast: H3_SAT_SLOTS slots of 16 words, 16 KiB.
+// One copy per GPU, held until the process ends; host code reaches it only through the device
+// address hipGetSymbolAddress returns (scratch_slots), never through its name.
+static __device__ __align__(256) unsigned long long scratch[H3_SAT_SLOTS * 16];
+
+int clear_sat_slots(unsigned long long *slots, hipStream_t stream, std::string *err) {
+    return clear_words(reinterpret_cast<uint32_t *>(slots), 2 * 16 * H3_SAT_SLOTS, stream, "clip counter", err);
+}
+
+int sat_total(const unsigned long long *slots, unsigned long long *sat, hipStream_t stream, std::string *err) {
+    hipLaunchKernelGGL(sat_total_kernel, dim3(1), dim3(64), 0, stream, slots, sat);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         *err = std::string("clip counter total launch failed: ") + hipGetErrorString(e);
         return H3_ELAUNCH;
     }
     return H3_OK;
+}
+
+bool scratch_slots(unsigned long long **slots, std::string *err) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static unsigned long long *addr[kMaxDevices];  // per device; null: not looked up yet
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = "no current HIP device (or a device index past 63)";
+        return false;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = std::string("scratch address lookup failed: ") + hipGetErrorString(e);
+            return false;
+        }
+        addr[dev] = static_cast<unsigned long long *>(p);
+    }
+    *slots = addr[dev];
+    return true;
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -551,16 +583,16 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
         return launch_kernel(reinterpret_cast<const void *>(kern), blocks, 0, p, stream, err);
     } else {
         auto kern = qk_kernel<D, IN, QT, KT, MODE, NN, VM>;
-        if (MODE == MODE_CAST && p.sat) {
-            const int rc = clear_words(reinterpret_cast<uint32_t *>(p.sat), 2 * H3_SAT_WORDS, stream, "clip counter", err);
+        if (MODE == MODE_CAST && p.sat_slots) {
+            const int rc = clear_sat_slots(p.sat_slots, stream, err);
             if (rc != H3_OK) return rc;
         }
         constexpr int threads = store_threads<D>(), wpb = threads / 64;  // waves (work items) per block
         const size_t lds = (size_t)(f.lds_per_cu / (kStoreWavesPerCU / wpb));
         const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + wpb - 1) / wpb, lds, p, stream,
                                      err, threads);
-        if (rc != H3_OK || MODE != MODE_CAST || !p.sat) return rc;
-        return sat_total(p.sat, stream, err);
+        if (rc != H3_OK || MODE != MODE_CAST || !p.sat_slots) return rc;
+        return sat_total(p.sat_slots, p.sat, stream, err);
     }
 }
 

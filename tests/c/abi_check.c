@@ -17,6 +17,8 @@ int main(void) {
     fails += rc != H3_EINVAL;
     rc = h3_qk_cast_e4m3_static(0, 0, H3_BF16, 0, 0, 0, 0, 0, 0, H3_E4M3FN, 0, 0);
     fails += rc != H3_EINVAL;
+    rc = h3_qk_cast_e4m3_static_noalloc(0, 0, H3_BF16, 0, 0, 0, 0, 0, 0, H3_E4M3FN, 0, 0);
+    fails += rc != H3_EINVAL;
     rc = h3_qk_rmsnorm_rope_permute_sage(0, 0, H3_F16, 0, 0, 0.125f, 0, 0, 0, 0);
     fails += rc != H3_EINVAL;
     rc = h3_qkv_amax(0, 0, H3_BF16, 0, 0, 0, 0);

@@ -211,6 +211,25 @@ def test_static_cast_validation():
     assert _static(d, v=BASE + 0x50000000, k=BASE + 0x50000000 + 32 * 2 * 128, sat=BASE + 0x61000001)[0] == "H3_EALIGN"
 
 
+def test_static_cast_noalloc_validation():
+    """The allocation-free static cast validates like h3_qk_cast_e4m3_static, with a three-word
+    counts output in place of the counter buffer (every case fails before any HIP call)."""
+    d = desc(D=128, pairs_per_axis=16)
+
+    def call(descale=BASE + 0x60000000, v=BASE + 0x50000000, v_dt=h3.E4M3FN, sat=BASE + 0x61000000):
+        with pytest.raises(h3.H3Error) as e:
+            h3.h3_qk_cast_e4m3_static_noalloc(d, BASE, h3.BF16, BASE + 0x20000000, BASE + 0x21000000, descale,
+                                              BASE + 0x30000000, BASE + 0x40000000, v, v_dt, sat, stream=0)
+        return e.value.name, h3.h3_last_error()
+    assert call(descale=0)[0] == "H3_EINVAL"
+    assert call(v_dt=h3.F32)[0] == "H3_EUNSUPPORTED"
+    assert call(sat=BASE + 0x61000004)[0] == "H3_EALIGN"
+    name, msg = call(sat=BASE + 0x60000000 - 16)  # the counts' last word on the first descale
+    assert name == "H3_EALIAS" and "sat_counts" in msg and "descale_qkv" in msg
+    name, msg = call(sat=BASE + 0x50000000 + 32 * 2 * 128 - 16)  # on the V codes' tail
+    assert name == "H3_EALIAS" and "sat_counts" in msg and "v_out" in msg
+
+
 def test_sage_validation():
     d = desc()
     def sage(scale=0.125, q=BASE + 0x30000000, k=BASE + 0x40000000, v=BASE + 0x50000000):
