@@ -392,23 +392,22 @@ __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, 
 }
 
 // RN(y / ds) without a division instruction, for a descale ds in [2^-60, 2^60] with
-// rcp = RN(1 / ds): q0 = RN(y rcp) is within 1.5 ulps of y / ds, one FMA remainder correction makes
-// it faithful, and a second one then gives the correctly rounded quotient (Markstein's theorem on
-// correcting a faithful quotient with a correctly rounded reciprocal; IBM J. Res. Dev. 34(1), 1990).
-// The remainders are taken negated, e = q ds - y (exact, like y - q ds), and enter the corrections
-// through the FMA's negation modifiers: the values are those of the plain form, and a zero y keeps
-// its sign through every step (-0 + -0 = -0 where the plain form's +0 remainder would give +0), so
-// no sign fix-up follows.  Checked against correctly rounded division for every finite binary32 y
-// and 64 descales: the same bits wherever |y / ds| is in [2^-12, 512), the same E4M3 code below
-// (quotients under 2^-11 may lose accuracy to underflow in the remainders, but every value under
-// 2^-10 encodes to a signed zero code), NaN or past 448 above.  The result is a correctly rounded
+// rcp = RN(1 / ds): q0 = RN(y rcp) is within one ulp of RN(y / ds), and one FMA remainder
+// correction, RN(q0 - (q0 ds - y) rcp), gives RN(y / ds) itself: the final step of Markstein's
+// division (IBM J. Res. Dev. 34(1), 1990), whose theorem asks for a correctly rounded reciprocal,
+// a starting quotient within one ulp of y / ds and an exact remainder.  q0 is not proven faithful
+// here; the sequence is instead checked against correctly rounded division for every pair of
+// significands of y and ds (2^46 quotients; exact power-of-two scaling carries that over to every
+// descale in the range and every quotient in [2^-12, 512)), and for every finite binary32 y at 80
+// descales: the same bits wherever |y / ds| is in [2^-12, 512), the same E4M3 code below (every
+// value under 2^-10 encodes to a signed zero code), NaN or past 448 above.  The remainder is taken
+// negated, e = q0 ds - y (exact, like y - q0 ds), and enters through the FMA's negation modifier:
+// a zero y keeps its sign (-0 + -0 = -0), with no fix-up.  The result is a correctly rounded
 // division, so the no-contraction rule of the arithmetic chain is untouched.
 __device__ __forceinline__ float quotient(float y, float ds, float rcp) {
     const float q0 = y * rcp;
     const float e0 = __builtin_fmaf(q0, ds, -y);
-    const float q1 = __builtin_fmaf(-e0, rcp, q0);
-    const float e1 = __builtin_fmaf(q1, ds, -y);
-    return __builtin_fmaf(-e1, rcp, q1);
+    return __builtin_fmaf(-e0, rcp, q0);
 }
 
 // A non-NaN quotient brought into the E4M3 range [-448, 448] (v_med3; +-inf included) ahead of the

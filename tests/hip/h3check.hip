@@ -2,7 +2,7 @@
 // operations they stand for, built with the library's own compiler flags (correctly rounded
 // division and square root, IEEE denormals, no contraction):
 //   - rsqrt_rn_large (row_rstd when eps >= 2^-96) against 1.0f / sqrtf(v);
-//   - quotient (the cast's RN(y / ds) from rcp = RN(1 / ds) and two FMA remainder corrections)
+//   - quotient (the cast's RN(y / ds) from rcp = RN(1 / ds) and one FMA remainder correction)
 //     against y / ds: every finite y at one descale, and every pair of significands;
 //   - the E4M3 encodings: the integer encoder f32_to_e4m3 written out for any range of bit
 //     patterns (the test compares it with the oracle on the host), the conversion instruction

@@ -1,5 +1,5 @@
 """The cast's quotient (quotient() in the library's device code: RN(y / ds) from rcp = RN(1 / ds),
-one product and two FMA remainder corrections) against correctly rounded division, on the GPU
+one product and one FMA remainder correction) against correctly rounded division, on the GPU
 through tests/hip/h3check.hip, built with the library's flags.
 
 - Every pair of significands: ds and y each over all 2^23 significands of [1, 2) (and -y for every
