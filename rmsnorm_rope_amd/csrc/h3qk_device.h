@@ -474,12 +474,9 @@ __device__ __forceinline__ void cast_e4m3_wave(const float (&y)[M][W], float ds,
     const bool bad = !(qm.m <= 448.0f);  // a quotient above 448 in magnitude or NaN
     bool exact = !fast, clip = false;
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-        bool nan = false;
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int k = 0; k < W; ++k) nan = nan || q[m][k] != q[m][k];
-        exact = exact || __builtin_amdgcn_ballot_w64(nan) != 0;
+        // the running maximum is NaN exactly when one of the lane's quotients is (one compare per
+        // lane instead of one per value: the clipping static cast 617 -> 597 us)
+        exact = exact || __builtin_amdgcn_ballot_w64(qm.m != qm.m) != 0;
         clip = true;
     }
     if (exact) {
