@@ -468,6 +468,50 @@ def bench_qk_tensors_2x1797(steps, warmup, rotate=8):
     return res
 
 
+def bench_tile_scaling(steps, warmup, rotate=8):
+    """The fixed cost of one store launch at decoder-tile sizes: the one-tile workload (token grid
+    31x16x16, H = 16, D = 64) and the same problem with its first T / 2 ... T / 16 tokens valid, each
+    over `rotate` buffer sets (inputs from HBM), launched back to back; a least-squares line
+    time = fixed + bytes / rate through the five points.  The full tile is also timed from a HIP
+    graph of 8 calls over the 8 sets (no host launch between the kernels)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth.problem import DeviceProblem, algorithmic_bytes
+    base = synth.workloads()["tile"]
+    stream = torch.cuda.current_stream()
+    pts = []
+    for div in (1, 2, 4, 8, 16):
+        t = base.T // div
+        wl = dataclasses.replace(base, T=t, valid=[t])
+        pbs = [DeviceProblem(wl, "cuda") for _ in range(rotate)]
+        outs = [(pb.out("f32"), pb.out("f16"), pb.out("f16")) for pb in pbs]
+        it = [0]
+
+        def launch():
+            j = it[0] % rotate
+            it[0] += 1
+            pbs[j].run_store("f32", "f16", outs=outs[j], stream=stream.cuda_stream)
+
+        per = time_interleaved({"x": launch}, steps, warmup, stream)["x"]
+        nb = algorithmic_bytes(wl, "store")
+        pts.append({"tokens": t, "bytes": nb, "us": round(per * 1e3, 2)})
+        if div == 1:
+            def graph_calls():
+                for j in range(rotate):
+                    pbs[j].run_store("f32", "f16", outs=outs[j])
+            g_ms = time_graph(graph_calls, calls=1, replays=max(10, steps // 2))
+            tile_graph_us = round(g_ms / rotate * 1e3, 2)
+        del pbs, outs
+    x = np.array([p["bytes"] for p in pts], float)
+    y = np.array([p["us"] for p in pts], float)
+    slope, fixed = np.polyfit(x, y, 1)
+    return {"points": pts, "fixed_us": round(float(fixed), 2), "rate_GBs": round(1e-3 / float(slope), 1),
+            "tile_graph_us_per_call": tile_graph_us,
+            "note": "least-squares line us = fixed + bytes / rate over the five sizes; 8 buffer sets rotated"}
+
+
 def bench_block_ops(steps, warmup, rotate=8):
     """SwiGLU on [1797, 2 x 8192] f16 and the scaled residual on [2 x 1797, 2048] (fp32 residual,
     f16 branch, per-channel scale), each with `rotate` buffer sets so the 256 MB MALL holds none."""
@@ -666,6 +710,7 @@ def main():
         extra["tensor_latent_k"] = bench_tensor(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
         extra["qk_tensors_2x1797x32x64"] = bench_qk_tensors_2x1797(max(20, args.steps), args.warmup)
         extra.update(bench_block_ops(max(20, args.steps), args.warmup))
+        extra["tile_scaling"] = bench_tile_scaling(max(20, args.steps), args.warmup)
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pb)
