@@ -264,11 +264,13 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
  * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,
  * SwiGLU row: SiluAndMul after the FP16 w1 output):
  *   x  DEVICE dt [N][2F] row-major: gate g = x[:, :F], up u = x[:, F:]
- *   y  DEVICE dt [N][F]:  y = RN_dt( s * u ), s = g / (1 + exp(-g)) in binary32
+ *   y  DEVICE dt [N][F]:  y = RN_dt(v), v = RN64(RN64(g / RN64(1 + exp(-g))) * u), the silu
+ *      product evaluated in binary64 and rounded once to dt (round to nearest even; NaN stays NaN,
+ *      its payload and sign not specified).
  * dt is H3_F16 or H3_BF16; F a multiple of 8; N * F / 8 < 2^32; x, y 16-byte aligned, not
- * overlapping.  exp and the reciprocal are the hardware binary32 approximations (relative error
- * below 1e-6); the f16 product s * u is rounded once to f16 (a mixed-precision FMA), the bf16 one
- * through binary32.  y may sit one ulp of dt from the exactly rounded value.
+ * overlapping.  Each element takes a binary32 evaluation when its rounding to dt is certain to be
+ * v's, and the binary64 evaluation otherwise (about one element in a thousand for data near zero,
+ * every element with |g| > 64).
  */
 int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream);
 

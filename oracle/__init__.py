@@ -419,12 +419,27 @@ def descale(amax: float) -> float:
 descale_of = descale
 
 
-def swiglu(x_bits: np.ndarray, in_dt: str = "f16") -> np.ndarray:
-    """x_bits [N, 2F] 16-bit -> y bits [N, F]: silu(gate) * up in binary64, one rounding."""
+def swiglu(x_bits: np.ndarray, in_dt: str = "f16", threads: int = 1) -> np.ndarray:
+    """x_bits [N, 2F] 16-bit -> y bits [N, F]: silu(gate) * up in binary64, one rounding.  With
+    threads > 1 the rows are split into contiguous blocks evaluated on host threads at once (the C
+    loop keeps no state, and ctypes releases the interpreter lock during the call)."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     N, F2 = x.shape
     y = np.empty((N, F2 // 2), np.uint16)
-    lib().h3ref_swiglu(_ptr(x), _ptr(y), N, F2 // 2, DT[in_dt])
+    L = lib()
+    cuts = [N * j // threads for j in range(threads + 1)]
+
+    def block(j):
+        a, b = cuts[j], cuts[j + 1]
+        if b > a:
+            L.h3ref_swiglu(_ptr(x[a:b]), _ptr(y[a:b]), b - a, F2 // 2, DT[in_dt])
+
+    if threads == 1:
+        block(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(block, range(threads)))
     return y
 
 

@@ -32,15 +32,99 @@ __device__ __forceinline__ uint32_t f32_to_h16(float x) {
     else return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// silu(g) u = (g / (1 + exp(-g))) u in binary32 with the hardware exp2 and reciprocal: a few
-// binary32 ulps in all (relative error below 1e-6), far under one ulp of the 16-bit output, so the
-// rounded result is the exactly rounded one except next to a rounding boundary, where it may be one
-// 16-bit ulp away.  exp(-g) overflows to +inf for g below about -88, giving silu = -0.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    const float e = __expf(-g);
+// ------------------------------------------------------------------ SwiGLU
+//
+// The contract: y = RN16(RN64(RN64(g / RN64(1 + exp(-g))) * u)), the binary64 evaluation rounded
+// once to the 16-bit output.  Each element takes a binary32 fast path whose result is used only when
+// its rounding to 16 bits is certain to be the contract's; otherwise it is evaluated in binary64.
+// Every (g, u) pair of either 16-bit dtype is checked against the CPU oracle by the tests.
+
+// exp(x) for |x| <= 64 in binary32, about one ulp: Cody and Waite's range reduction (W. J. Cody,
+// W. Waite, Software Manual for the Elementary Functions, 1980), x = k ln2 + r with |r| <= ln2 / 2,
+// ln2 split in two so that k ln2_hi is exact (ln2_hi has 15 significant bits, |k| <= 93), then the
+// degree-7 Taylor polynomial of exp(r) (truncation below 2^-26 relative) and a scaling by 2^k.
+__device__ __forceinline__ float exp_reduced(float x) {
+    constexpr float kLog2e = 1.44269504088896340736f;
+    constexpr float kLn2Hi = 0.693145751953125f;         // ln 2 to 15 bits
+    constexpr float kLn2Lo = 1.42860676533018700e-06f;    // ln 2 - kLn2Hi, rounded
+    const float k = __builtin_rintf(x * kLog2e);
+    float r = __builtin_fmaf(k, -kLn2Hi, x);              // exact
+    r = __builtin_fmaf(k, -kLn2Lo, r);
+    float p = 1.0f / 5040.0f;
+    p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)k);
+}
+
+// The value as a materialised binary32 (the compiler may otherwise fold a product and its
+// conversion to binary16 into one mixed-precision FMA).
+__device__ __forceinline__ float keep32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// binary64 -> 16-bit float (FRAC fraction bits, smallest normal exponent EMIN, INF / NAN codes) with
+// one rounding to nearest even; the conversion instructions go through binary32 and round twice.
+template <int FRAC, int EMIN, uint32_t INF, uint32_t QNAN>
+__device__ __forceinline__ uint32_t round_f64_to_16(double v) {
+    const uint64_t x = (uint64_t)__double_as_longlong(v);
+    const uint32_t sign = (uint32_t)(x >> 48) & 0x8000u;
+    const uint64_t a = x & 0x7FFFFFFFFFFFFFFFull;
+    if (a > 0x7FF0000000000000ull) return sign | QNAN;
+    const int E = (int)(a >> 52);
+    const uint64_t sig = (a & 0xFFFFFFFFFFFFFull) | (E ? (1ull << 52) : 0ull);
+    const int e = E ? E - 1023 : -1022;
+    if (e > (int)(INF >> FRAC) + EMIN - 1) return sign | INF;
+    const int shift = 52 - FRAC + (e < EMIN ? EMIN - e : 0);
+    if (shift > 63) return sign;  // below half the smallest subnormal: rounds to zero
+    uint64_t q = sig >> shift;
+    const uint64_t rem = sig & ((1ull << shift) - 1ull), half = 1ull << (shift - 1);
+    q += (rem > half || (rem == half && (q & 1ull))) ? 1ull : 0ull;
+    uint64_t code = (e > EMIN ? (uint64_t)(e - EMIN) << FRAC : 0ull) + q;
+    if (code >= INF) code = INF;
+    return sign | (uint32_t)code;
+}
+
+// The contract's binary64 evaluation.
+template <int DT>
+__device__ uint32_t silu_mul_f64(float g, float u) {
+    const double gd = g, ud = u;
+    const double s = gd / (1.0 + exp(-gd));
+    const double v = s * ud;
+    if constexpr (DT == H3_BF16) return round_f64_to_16<7, -126, 0x7F80u, 0x7FC0u>(v);
+    else return round_f64_to_16<10, -14, 0x7C00u, 0x7E00u>(v);
+}
+
+// Fast path.  y = RN32(RN32(g * rcp(RN32(1 + e))) * u) with e = exp_reduced(-g) is within a few
+// binary32 ulps of the exact silu(g) u (about 1.5 ulp from e, 0.5 from the sum, 1 from the
+// hardware reciprocal, 0.5 from each product; over every (g, u) pair of either dtype with
+// |g| <= 64 it was never more than 3 ulps from the binary64 value rounded to binary32), and the
+// contract's binary64 value is within 2^-50 of the exact one.  So the 16-bit rounding of y is the
+// contract's unless a 16-bit rounding boundary lies within that distance of y: the element is
+// taken here only when |g| <= 64 and y is zero, or lies in the 16-bit normal range more than
+// kNearUlps binary32 ulps from every boundary (there the boundaries are the binary32 values whose
+// bits below the 16-bit fraction hold the midpoint pattern, evenly spaced in the bit patterns).
+// Otherwise ok is false and the caller evaluates the element in binary64.
+constexpr uint32_t kNearUlps = 4;
+
+template <int DT>
+__device__ __forceinline__ uint32_t silu_mul_fast(float g, float u, bool &ok) {
+    const float e = exp_reduced(-g);
     const float d = 1.0f + e;
     const float s = g * __builtin_amdgcn_rcpf(d);
-    return s * u;
+    const float y = keep32(s * u);
+    const uint32_t a = __float_as_uint(y) & 0x7FFFFFFFu;
+    constexpr uint32_t kLow = DT == H3_BF16 ? 0xFFFFu : 0x1FFFu;          // bits below the 16-bit fraction
+    constexpr uint32_t kMid = (kLow >> 1) + 1u;                            // their midpoint pattern
+    constexpr uint32_t kMinNormal = DT == H3_BF16 ? 0x00800000u : 0x38800000u;
+    const bool far = ((a & kLow) - (kMid - kNearUlps)) > 2u * kNearUlps;
+    ok = (__builtin_fabsf(g) <= 64.0f) & ((a == 0u) | ((a >= kMinNormal) & far));  // no branches
+    return f32_to_h16<DT>(y);
 }
 
 template <int DT>
@@ -54,14 +138,23 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *__restrict_
     const uint16_t *row = x + (uint64_t)n * (2u * (uint64_t)F);
     const u32x4 gv = *reinterpret_cast<const u32x4 *>(row + f);
     const u32x4 uv = *reinterpret_cast<const u32x4 *>(row + F + f);
-    uint32_t o[4];
+    uint32_t o[8];
+    bool ok[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float y0 = silu_mul(h16_to_f32<DT>(gv[k] & 0xFFFFu), h16_to_f32<DT>(uv[k] & 0xFFFFu));
-        const float y1 = silu_mul(h16_to_f32<DT>(gv[k] >> 16), h16_to_f32<DT>(uv[k] >> 16));
-        o[k] = f32_to_h16<DT>(y0) | (f32_to_h16<DT>(y1) << 16);
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t gb = (k & 1) ? (gv[k >> 1] >> 16) : (gv[k >> 1] & 0xFFFFu);
+        const uint32_t ub = (k & 1) ? (uv[k >> 1] >> 16) : (uv[k >> 1] & 0xFFFFu);
+        o[k] = silu_mul_fast<DT>(h16_to_f32<DT>(gb), h16_to_f32<DT>(ub), ok[k]);
     }
-    __builtin_nontemporal_store((u32x4){o[0], o[1], o[2], o[3]},
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (!ok[k]) {  // rare: binary64 for this element (the lanes that need it)
+            const uint32_t gb = (k & 1) ? (gv[k >> 1] >> 16) : (gv[k >> 1] & 0xFFFFu);
+            const uint32_t ub = (k & 1) ? (uv[k >> 1] >> 16) : (uv[k >> 1] & 0xFFFFu);
+            o[k] = silu_mul_f64<DT>(h16_to_f32<DT>(gb), h16_to_f32<DT>(ub));
+        }
+    }
+    __builtin_nontemporal_store((u32x4){o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)},
                                 reinterpret_cast<u32x4 *>(y + (uint64_t)t * 8u));
   }
 }

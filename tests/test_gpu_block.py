@@ -1,7 +1,8 @@
 """GPU parity of the decoder-block elementwise ops (SwiGLU, scaled residual) against the oracle,
-through the C ABI.  Scaled residual: bit-exact.  SwiGLU: the oracle rounds the binary64 value once;
-the GPU evaluates in binary32 with the device exp, so a result may sit one ulp of the 16-bit output
-away; such elements are counted and must stay rare (< 1 %), never more than one ulp."""
+through the C ABI, bit for bit: the scaled residual in binary32 with the product rounded first;
+SwiGLU as the binary64 value rounded once to the 16-bit output (the kernel's binary32 fast path is
+used only where its rounding is certain; tests/test_gpu_swiglu_exhaustive.py covers every input
+pair).  NaN outputs match any NaN."""
 import numpy as np
 import pytest
 
@@ -39,9 +40,8 @@ def test_swiglu(N, F, dt):
     xb = synth.swiglu_input(N, F, dt)
     got = run_swiglu(xb, dt)
     ref = oracle.swiglu(xb, dt)
-    hist = compare(got, ref, dt, "swiglu", max_ulp=1)
+    hist = compare(got, ref, dt, "swiglu")
     print("swiglu", N, F, dt, "ulp histogram", hist, flush=True)
-    assert hist[1] <= 0.01 * got.size
 
 
 def test_swiglu_special_values():
@@ -52,7 +52,7 @@ def test_swiglu_special_values():
     x[1, 8:] = [1.0, 1.0, 1.0, np.inf, 0.0, -0.0, 2.0, 1e-3]
     got = run_swiglu(x.view(np.uint16), "f16")
     ref = oracle.swiglu(x.view(np.uint16), "f16")
-    compare(got, ref, "f16", "swiglu specials", max_ulp=1)
+    compare(got, ref, "f16", "swiglu specials")
 
 
 def run_residual(res, br, sc, dt):

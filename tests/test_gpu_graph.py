@@ -1,8 +1,9 @@
 """The entry points are graph-capturable: every pass is plain kernel launches on the caller's stream
 (the amax and clip-counter clears are kernels, not memset nodes).  A HIP graph holding the store,
-amax, cast, static cast with counters, one-tensor and sage passes is replayed several times, with
-eager work and the outputs overwritten between replays; every replay must reproduce the eager
-results bit for bit."""
+amax, cast, static cast with counters (also its allocation-free form, whose partial counts live in
+the library's static scratch), one-tensor and sage passes is replayed several times, with eager work
+and the outputs overwritten between replays; every replay must reproduce the eager results bit for
+bit."""
 import dataclasses
 
 import numpy as np
@@ -48,6 +49,8 @@ def test_graph_replays_match_eager():
             "cast": (pb.out("e4m3"), pb.out("e4m3"), pb.out("bf16"), torch.empty(2, dtype=torch.float32, device="cuda")),
             "static": (pb.out("e4m3"), pb.out("e4m3"), pb.out("e4m3"),
                        torch.empty(h3.SAT_WORDS, dtype=torch.int64, device="cuda")),
+            "static_noalloc": (pb.out("e4m3"), pb.out("e4m3"), pb.out("e4m3"),
+                               torch.empty(3, dtype=torch.int64, device="cuda")),
             "tensor": torch.empty((wl64.B, wl64.T, H, D), dtype=torch.float16, device="cuda"),
             "sage": (pb64.out("f32"), pb64.out("f32"), pb64.out("f16")),
         }
@@ -57,6 +60,9 @@ def test_graph_replays_match_eager():
         pb.run_amax(o["amax"], stream=stream)
         pb.run_cast(o["amax"], outs=o["cast"], stream=stream)
         pb.run_cast_static(ds, v_fp8=True, outs=o["static"], stream=stream)
+        q8, k8, v8, cnt = o["static_noalloc"]
+        h3.h3_qk_cast_e4m3_static_noalloc(pb.desc, pb.qkv, pb.in_dt, pb.wq, pb.wk, ds, q8, k8, v8, "e4m3", cnt,
+                                          stream=stream)
         h3.h3_tensor_norm_rope(tdesc, kptr, "f16", pb64.wk, o["tensor"], "f16", h3.LAYOUT_BTHD, stream=stream)
         pb64.run_sage(0.125, outs=o["sage"], stream=stream)
 
@@ -71,6 +77,7 @@ def test_graph_replays_match_eager():
     run_all(eager)
     torch.cuda.synchronize()
     ref = snapshot(eager)
+    assert np.array_equal(eager["static"][3][:3].cpu().numpy(), eager["static_noalloc"][3].cpu().numpy())
 
     graphed = make_outs()
     run_all(graphed)  # warm up outside the capture (first-call device queries)
