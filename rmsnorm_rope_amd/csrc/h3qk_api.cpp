@@ -25,7 +25,8 @@ struct Range {
 };
 
 // The address ranges of one call's inputs or outputs, held in place: validation of a call that
-// succeeds allocates no memory.  A call has at most 6 inputs and 5 outputs.
+// succeeds allocates no memory.  A call has at most 6 inputs and 5 outputs; a list that would hold
+// more than its capacity records that, and the overlap checks then fail the call (check_outputs).
 class RangeList {
   public:
     RangeList() = default;
@@ -34,7 +35,9 @@ class RangeList {
     }
     void push_back(const Range &r) {
         if (n_ < kCap) r_[n_++] = r;
+        else overflow_ = true;
     }
+    bool overflow() const { return overflow_; }
     size_t size() const { return (size_t)n_; }
     const Range &operator[](size_t i) const { return r_[i]; }
     const Range *begin() const { return r_; }
@@ -44,6 +47,7 @@ class RangeList {
     static constexpr int kCap = 8;
     Range r_[kCap];
     int n_ = 0;
+    bool overflow_ = false;
 };
 
 bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
@@ -147,6 +151,7 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
 }
 
 int check_outputs(const RangeList &inputs, const RangeList &outputs) {
+    if (inputs.overflow() || outputs.overflow()) return fail(H3_EINVAL, "internal: too many buffers to check for overlap");
     for (size_t i = 0; i < outputs.size(); ++i) {
         if (!aligned16(reinterpret_cast<const void *>(outputs[i].lo)))
             return fail(H3_EALIGN, std::string(outputs[i].name) + " must be 16-byte aligned");
