@@ -262,7 +262,7 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
 
 /*
  * SwiGLU on the 16-bit output of a decoder block's w1 projection ([OMNI-6607] Operations table,
- * SwiGLU row: SiluAndMul after the FP16 w1 output):
+ * SwiGLU row: silu of the gate half times the up half of the FP16 w1 projection output):
  *   x  DEVICE dt [N][2F] row-major: gate g = x[:, :F], up u = x[:, F:]
  *   y  DEVICE dt [N][F]:  y = RN_dt(v), v = RN64(RN64(g / RN64(1 + exp(-g))) * u), the silu
  *      product evaluated in binary64 and rounded once to dt (round to nearest even; NaN stays NaN,

@@ -588,7 +588,7 @@ int h3ref_qk_sage(const h3ref_problem *P, const void *qkv, int in_dt, const floa
 
 /* ------------------------------------------------------------------ decoder-block elementwise ops
  * vllm-omni PR #6607, "Operations" table, SwiGLU and scaled-residual rows (and the B300 isolated
- * measurements in the review thread): SwiGLU is SiluAndMul applied to the FP16 output of w1 (gate =
+ * measurements in the review thread): SwiGLU is the silu-and-multiply of the FP16 output of w1 (gate =
  * first half of the last dim, up = second half); the scaled residual is an FP32 residual plus the
  * FP16 branch times an FP32 scale, with contraction disabled.
  */

@@ -1,9 +1,9 @@
 """SwiGLU (h3_swiglu, through the C ABI) against the CPU oracle for every (gate, up) pair of 16-bit
 values: 2^32 pairs per dtype, f16 and bf16, so the kernel's binary32 fast path and its decision to
 fall back to binary64 are checked on the whole input domain.  The op is [OMNI-6607]'s SwiGLU
-(vllm-omni PR #6607, "Operations" table, SwiGLU row: SiluAndMul on the FP16 w1 output), computed as
-silu(g) * u in binary64 and rounded once to the output dtype; NaN outputs match any NaN (payloads
-are not part of the contract).
+(vllm-omni PR #6607, "Operations" table, SwiGLU row: the gate's silu times the up half, taken on the
+FP16 output of the w1 projection), computed as silu(g) * u in binary64 and rounded once to the
+output dtype; NaN outputs match any NaN (payloads are not part of the contract).
 
 Each call covers 4096 gate values (one per row, repeated across the row's F = 65536 gate columns)
 against all 65536 up values; the oracle runs on the host threads at the same time."""
