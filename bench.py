@@ -202,6 +202,26 @@ def bench_store(wl, steps, warmup, rotate=1):
     return pbs[0], {"ms_per_step": total / steps, "kernel_ms": per, "bytes": nbytes}
 
 
+def bench_store_dtypes(wl, steps, warmup, combos=(("bf16", "bf16"), ("f32", "bf16"), ("f32", "f32"))):
+    """The store pass on one workload for several (Q, K) output dtypes (V keeps the input dtype),
+    timed in turn; returns one entry per combination."""
+    import torch
+
+    from synth.problem import DeviceProblem, algorithmic_bytes
+    pb = DeviceProblem(wl, "cuda")
+    stream = torch.cuda.current_stream()
+    outs = {c: (pb.out(c[0]), pb.out(c[1]), pb.out(wl.in_dtype)) for c in combos}
+    launches = {f"{q}/{k}": (lambda c=(q, k): pb.run_store(c[0], c[1], outs=outs[c], stream=stream.cuda_stream))
+                for q, k in combos}
+    per = time_interleaved(launches, steps, warmup, stream)
+    res = {}
+    for q, k in combos:
+        ms, nbytes = per[f"{q}/{k}"], algorithmic_bytes(wl, "store", q, k)
+        res[f"q_{q}_k_{k}"] = {"us_per_call": round(ms * 1e3, 2), "GBs": round(nbytes / ms / 1e6, 1),
+                               "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+    return res
+
+
 def bench_fp8(wl, steps, warmup):
     import torch
 
@@ -703,6 +723,8 @@ def main():
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
         shard = dataclasses.replace(synth.workloads()["fp8long"], T=13056, valid=[13056])
         extra["fp8long_shard8"] = bench_fp8(shard, max(10, args.steps // 2), args.warmup)
+        extra["fp8long_store"] = bench_store_dtypes(synth.workloads()["fp8long"], max(10, args.steps // 2),
+                                                    args.warmup)
         extra["fp8long_shard8"]["note"] = "one of 8 sequence shards (T = 13,056), uncounted"
         extra["fp8long_tensor_k"] = bench_tensor_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2),
                                                      args.warmup)

@@ -67,8 +67,12 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
         for (int u = 0; u < HPW; ++u) {
             if (u >= nh) break;
             const int64_t o = obase + u * p.out_hstride;
+            if constexpr (kF32PairStore<OT, W, M>) {
+                store_f32_zero_row_pairs(p.q, o + olane, c);
+            } else {
 #pragma unroll
-            for (int m = 0; m < M; ++m) store_zero_chunk<OT, W>(p.q, o + (olane + 8 * W * m + W * c));
+                for (int m = 0; m < M; ++m) store_zero_chunk<OT, W>(p.q, o + (olane + 8 * W * m + W * c));
+            }
         }
         return;
     }
@@ -131,6 +135,8 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
         } else {
             if constexpr (kPairStore<OT, W, M>) {
                 store_row_pairs<OT, W>(p.q, o + olane, c, x[u]);
+            } else if constexpr (kF32PairStore<OT, W, M>) {
+                store_f32_row_pairs<W>(p.q, o + olane, c, x[u]);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) store_chunk<OT, W>(p.q, o + (olane + 8 * W * m + W * c), x[u][m]);

@@ -219,6 +219,51 @@ __device__ __forceinline__ void store_code_words(void *base, int64_t e, const ui
 template <int OT, int W, int M>
 constexpr bool kPairStore = M == 2 && (OT == DT_F16 || OT == DT_BF16) && W == 4;
 
+// Binary32 rows at W = 8, M = 2 (a chunk is 32 bytes, two 16-byte halves).  Chunk j < 4 (lane j) and
+// chunk j + 4 (its half-mirror lane 7 - j) trade halves, so that each of the row's four store
+// instructions writes one whole 128-byte quarter of the row across the token's 8 lanes: the low
+// lane writes its own first half, then the high lane's first half (32 floats further on); the high
+// lane writes the low lane's second half, then its own second half.  Stored chunk by chunk, every
+// instruction would write half of each of two lines (measured on the FP8 long-sequence shape with
+// binary32 Q and K: 1183 us per store pass).
+template <int OT, int W, int M>
+constexpr bool kF32PairStore = M == 2 && OT == DT_F32 && W == 8;
+
+// Element offset, from the row's start, of the lane's first 16-byte store for chunk c.
+__device__ __forceinline__ uint32_t f32_pair_offset(int c) { return 8u * (uint32_t)(c & 3) + ((c & 4) ? 4u : 0u); }
+
+// `src` from the half-mirror lane for the lanes of the DPP banks in BANKS (4-lane groups of a
+// 16-lane row: 0x5 = lanes 0-3 of each 8, 0xA = lanes 4-7); the other lanes keep `old`.
+template <int BANKS>
+__device__ __forceinline__ float mirror8_into(float old, float src) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), 0x141, 0xF, BANKS, false));
+}
+
+template <int W>
+__device__ __forceinline__ void store_f32_row_pairs(void *base, int64_t row_e, int c, const float (&y)[2][W]) {
+    static_assert(W == 8, "32-byte chunks");
+    float *p = reinterpret_cast<float *>(base) + row_e + f32_pair_offset(c);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        f32x4 a, b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[k] = mirror8_into<0xA>(y[m][k], y[m][k + 4]);  // high lanes: the low lane's second half
+            b[k] = mirror8_into<0x5>(y[m][k + 4], y[m][k]);  // low lanes: the high lane's first half
+        }
+        st_nt(reinterpret_cast<f32x4 *>(p + 64 * m), a);
+        st_nt(reinterpret_cast<f32x4 *>(p + 64 * m + 32), b);
+    }
+}
+
+// A zero binary32 row at W = 8, M = 2, with the same whole-line stores.
+__device__ __forceinline__ void store_f32_zero_row_pairs(void *base, int64_t row_e, int c) {
+    float *p = reinterpret_cast<float *>(base) + row_e + f32_pair_offset(c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st_nt(reinterpret_cast<f32x4 *>(p + 32 * q), (f32x4){0.f, 0.f, 0.f, 0.f});
+}
+
 // ------------------------------------------------------------------ the row
 
 // One Q or K head row is held as x[m][k] (dim 8W m + W c + k, c the lane's chunk).  Binary32,

@@ -108,10 +108,17 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
         for (int u = 0; u < HPW; ++u) {
             if (u >= nh) break;
             const int64_t o = obase + u * plane;
+            if constexpr (kF32PairStore<QT, W, M>) {
+                store_f32_zero_row_pairs(p.q, o + olane, c);
+            } else {
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                store_zero_chunk<QT, W>(p.q, o + (olane + 8 * W * m + W * c));
-                store_zero_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c));
+                for (int m = 0; m < M; ++m) store_zero_chunk<QT, W>(p.q, o + (olane + 8 * W * m + W * c));
+            }
+            if constexpr (kF32PairStore<KT, W, M>) {
+                store_f32_zero_row_pairs(p.k, o + olane, c);
+            } else {
+#pragma unroll
+                for (int m = 0; m < M; ++m) store_zero_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c));
             }
             if constexpr (VF8) {  // D bytes per token row: 8 or 16 bytes per lane
                 if constexpr (VC == 2)
@@ -258,12 +265,16 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
             }
             if constexpr (kPairStore<QT, W, M>) {
                 store_row_pairs<QT, W>(p.q, o + olane, c, xq);
+            } else if constexpr (kF32PairStore<QT, W, M>) {
+                store_f32_row_pairs<W>(p.q, o + olane, c, xq);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) store_chunk<QT, W>(p.q, o + (olane + 8 * W * m + W * c), xq[m]);
             }
             if constexpr (kPairStore<KT, W, M>) {
                 store_row_pairs<KT, W>(p.k, o + olane, c, xk);
+            } else if constexpr (kF32PairStore<KT, W, M>) {
+                store_f32_row_pairs<W>(p.k, o + olane, c, xk);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) store_chunk<KT, W>(p.k, o + (olane + 8 * W * m + W * c), xk[m]);

@@ -91,7 +91,7 @@ def test_store_small(name, kw):
 @pytest.mark.parametrize("in_dt", ["f16", "bf16"])
 def test_store_dtype_matrix(q_dt, k_dt, in_dt):
     check_store(W("tiny", T=40, grid=(2, 4, 5), B=2, valid=[40, 31], in_dtype=in_dt), q_dt, k_dt)
-    check_store(W("tiny", T=12, grid=(1, 3, 4), D=128, n=16, in_dtype=in_dt), q_dt, k_dt)
+    check_store(W("tiny", T=12, grid=(1, 3, 4), B=2, valid=[12, 5], D=128, n=16, in_dtype=in_dt), q_dt, k_dt)
 
 
 def test_store_max_row_stride():
@@ -327,6 +327,15 @@ def test_full_fp8long():
     say(f"[full] fp8long amax {ra.tolist()}")
 
 
+def test_full_fp8long_store_f32():
+    """The store pass on the full long sequence with binary32 Q and K (whole-line binary32 rows at
+    D = 128), every output element against the oracle."""
+    wl = synth.workloads()["fp8long"]
+    pb = DeviceProblem(wl, "cuda")
+    hq, hk = check_store(wl, "f32", "f32", pb=pb)
+    say(f"[full] fp8long store f32/f32: Q ulp histogram {hq}, K {hk}")
+
+
 # ----------------------------------------------------------------------------- determinism / streams
 
 def test_repeat_and_side_stream():
@@ -350,3 +359,4 @@ def test_generator_on_device_matches_host():
     dev = synth.qkv_device(wl, "cuda")[0, 1000:1100].cpu().numpy().view(np.uint16)
     host = synth.qkv_host(wl, np.arange(1000, 1100))
     assert np.array_equal(dev, host)
+

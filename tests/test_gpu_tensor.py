@@ -185,7 +185,7 @@ TENSOR_CASES = [
 def test_tensor_store(name, kw, slot):
     wl = W(name, **kw)
     tc = TensorCase(wl, slot, compact=False)
-    for out_dt, layout in (("f32", 0), ("f16", 1), ("bf16", 0), ("bf16", 1)):
+    for out_dt, layout in (("f32", 0), ("f32", 1), ("f16", 1), ("bf16", 0), ("bf16", 1)):
         check_tensor_store(tc, out_dt, layout)
     check_tensor_store(TensorCase(wl, slot, compact=True), "f16", 1)
 
