@@ -128,6 +128,8 @@ __global__ __launch_bounds__(256) void tensor_kernel(const QkParams p) {
             cast_e4m3_wave<M, W>(x[u], ds, rcp, fast, p.sat_slots != nullptr, nsat, cw);
             if constexpr (W == 8 && M == 2) {
                 store_words_pairs<1, W>(p.q, o + olane, c, cw[0], cw[1]);
+            } else if constexpr (W == 4 && M == 2) {
+                store_word_pairs(p.q, o + olane, c, cw[0][0], cw[1][0]);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) store_code_words<W>(p.q, o + (olane + 8 * W * m + W * c), cw[m]);

@@ -197,6 +197,17 @@ __device__ __forceinline__ void store_words_pairs(void *base, int64_t row_e, int
     st_nt(reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(base) + e * EB), v);
 }
 
+// The same trade for 4-byte chunks (E4M3 codes with W = 4, one word per chunk): one 8-byte store per
+// lane writes the token's 64-byte row whole, and the wave's 8 tokens 512 contiguous bytes.
+__device__ __forceinline__ void store_word_pairs(void *base, int64_t row_e, int c, uint32_t m0, uint32_t m1) {
+    const bool odd = c & 1;
+    const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? m0 : m1), 0xB1, 0xF, 0xF, true);
+    const u32x2 v = odd ? (u32x2){r, m1} : (u32x2){m0, r};
+    // even chunk 2j: bytes [8j, 8j + 8); odd chunk 2j + 1: [32 + 8j, 32 + 8j + 8)
+    const int64_t e = row_e + (odd ? 32 + 4 * (c - 1) : 4 * c);
+    st_nt(reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(base) + e), v);
+}
+
 template <int OT, int W>
 __device__ __forceinline__ void store_row_pairs(void *base, int64_t row_e, int c, const float (&y)[2][W]) {
     static_assert((OT == DT_F16 || OT == DT_BF16) && W == 4, "16-bit outputs, 4-wide chunks");

@@ -249,6 +249,9 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
             if constexpr (W == 8 && M == 2) {
                 store_words_pairs<1, W>(p.q, o + olane, c, cw[0][0], cw[0][1]);
                 store_words_pairs<1, W>(p.k, o + olane, c, cw[1][0], cw[1][1]);
+            } else if constexpr (W == 4 && M == 2) {
+                store_word_pairs(p.q, o + olane, c, cw[0][0][0], cw[0][1][0]);
+                store_word_pairs(p.k, o + olane, c, cw[1][0][0], cw[1][1][0]);
             } else {
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
