@@ -55,15 +55,25 @@ enum Mode : int { MODE_STORE = 0, MODE_AMAX = 1, MODE_CAST = 2 };
 constexpr int kHeadsPerWave = 2;  // heads of one 8-token group served by one wave (fused Q, K, V)
 constexpr int kTensorHeads = 4;   // the same for one separately projected tensor
 
-// Resident blocks per CU of the streaming store / cast kernels (a cap imposed through LDS): 3 for
-// the fused kernels, 4 for the one-tensor kernels, whose waves move fewer bytes each (measured on
-// the full latent's K heads: 3 blocks 234 us, 4 blocks 175 us, 6-8 blocks within 1 % of 4).
-// Store / cast blocks: at most 12 resident waves per CU, in blocks of 8 tokens x 8 heads for D = 64
-// (4 waves) and 8 tokens x 4 heads for D = 128 (2 waves), i.e. 12,288 16-bit input values (24 KiB)
-// per block either way.
-constexpr int kStoreWavesPerCU = 12;
-template <int D>
-constexpr int store_threads() { return D == 64 ? 256 : 128; }
+// Launch geometry of the fused store / cast kernels: threads per block (one 8-token work item per
+// wave) and the most resident waves per CU (a cap imposed through LDS).  Measured per pass:
+//   * D = 64 store: 4-wave blocks (8 tokens x 8 heads), 12 waves per CU (the full latent: 616 us;
+//     8 waves 630, 16-20 waves 636-651, 2-wave blocks 629-632).
+//   * D = 64 cast: 4-wave blocks, 24 waves per CU (every wave its VGPRs allow): its arithmetic
+//     wants more waves in flight (the full latent, V copied: 12 waves 530 us, 16 474, 20-24 460;
+//     V codes: 632, 479 and 458-467).
+//   * D = 128 store: 6 waves per CU, in 2-wave blocks (8 tokens x 4 heads) for 16-bit Q and K and in
+//     1-wave blocks when Q or K is binary32 (the FP8 long-sequence shape: bf16 / bf16 at 12 waves
+//     691-695 us, at 4-6 waves 669-676; f32 / f32 in 2-wave blocks 973-981, in 1-wave blocks 930-935;
+//     f32 / bf16 840-849 and 812-817).
+//   * D = 128 cast: 2-wave blocks, 12 waves per CU (8 waves 624 us, 12 580-584, 16 587; 1-wave
+//     blocks 600).
+template <int D, bool CAST, bool F32OUT>
+constexpr int store_threads() { return D == 64 ? 256 : (!CAST && F32OUT) ? 64 : 128; }
+template <int D, bool CAST>
+constexpr int store_waves_per_cu() { return D == 64 ? (CAST ? 24 : 12) : (CAST ? 12 : 6); }
+// Resident blocks per CU of the one-tensor kernels: 4, their waves moving fewer bytes each
+// (measured on the full latent's K heads: 3 blocks 234 us, 4 blocks 175 us, 6-8 within 1 % of 4).
 constexpr int kTensorBlocksPerCU = 4;
 
 // Everything a QK kernel reads, passed by value in the kernel arguments (< 1.5 KiB).

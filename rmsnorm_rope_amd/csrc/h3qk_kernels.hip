@@ -15,15 +15,15 @@
 //     then xor 2, then xor 1), levels below W fold inside the chunk.  Floating-point addition is
 //     commutative, so the butterfly partner computes the same bits as the tree node, and all
 //     8 lanes end with ss.
-//   * Store and cast passes: one work item per wave, one short-lived block per 8 tokens x 8 heads
-//     (D = 64, 4 waves) or 8 tokens x 4 heads (D = 128, 2 waves), 24 KiB of input either way.
+//   * Store and cast passes: one work item per wave, short-lived blocks of 1 to 4 waves (8 tokens x
+//     2 to 8 heads; the geometry is chosen per pass, see store_threads).
 //     Blocks are dispatched in order, so the chip writes a narrow sliding window of
 //     each head plane of the [B, H, T, D] outputs; on MI355X that keeps HBM write efficiency
 //     well above a persistent grid-stride sweep, which holds a window of every plane open.
 //     Each wave issues its data loads first, stores V (which needs nothing from Q and K) as soon
 //     as it arrives, then decodes positions and fetches weights and rotary entries.  Outputs are
 //     written once and never read back, so they bypass the caches (nontemporal stores), each row
-//     as whole 128-byte lines.  At most 12 waves are resident per CU (see kStoreWavesPerCU).
+//     as whole 128-byte lines.  Resident waves per CU are capped per pass (store_waves_per_cu).
 //   * Amax pass: persistent waves over the work items with the next item's loads in flight
 //     while the current one is reduced, one atomic max per block and tensor.  It stores nothing,
 //     so it always takes W = 4 (M = D / 32), which keeps the cross-lane tree levels at 12 DPP adds
@@ -555,7 +555,8 @@ bool resident_blocks(const void *kern, const DeviceFacts &f, int *blocks, std::s
 int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hipStream_t stream, std::string *err,
                   int threads) {
     if (blocks <= 0) return H3_OK;
-    if (blocks > 0x7FFFFFFF) {
+    // the dispatch's grid is a 32-bit count of work-items
+    if ((uint64_t)blocks * (uint64_t)threads > 0xFFFFFFFFull) {
         *err = "problem too large for one launch";
         return H3_EUNSUPPORTED;
     }
@@ -570,14 +571,11 @@ int launch_kernel(const void *kern, int64_t blocks, size_t lds, QkParams &p, hip
 
 namespace {
 
-// Launch geometry of the store / cast kernels (store_threads, kStoreWavesPerCU).  They stream with
-// no reuse, and on MI355X fewer and smaller concurrent blocks keep a narrower window of every output
-// plane open in HBM: 12 waves per CU measured best for the full-latent workload (D = 64; 16-20
-// waves within 1 %, 24-28 about 7 % slower), in 4-wave blocks there (2-wave blocks: 632 against
-// 620 us; 1-wave blocks: 652), and in 2-wave blocks for D = 128 (against 4-wave blocks on the FP8
-// long sequence: cast 606 -> 588 us, cast with V codes 613 -> 576 us, 16-bit store 933 -> 917 us).
-// The cap is imposed by reserving the matching share of the CU's LDS per block (the kernels use
-// none).
+// Launch geometry of the store / cast kernels (store_threads, store_waves_per_cu).  They stream
+// with no reuse, and on MI355X fewer and smaller concurrent blocks keep a narrower window of every
+// output plane open in HBM; the casts, which do more arithmetic per byte, want more waves in flight
+// where their registers allow.  The cap is imposed by reserving the matching share of the CU's LDS
+// per block (the kernels use none).
 
 template <int D, int IN, int QT, int KT, int MODE, int NN, int VM>
 int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
@@ -601,8 +599,11 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
             const int rc = clear_sat_slots(p.sat_slots, stream, err);
             if (rc != H3_OK) return rc;
         }
-        constexpr int threads = store_threads<D>(), wpb = threads / 64;  // waves (work items) per block
-        const size_t lds = (size_t)(f.lds_per_cu / (kStoreWavesPerCU / wpb));
+        constexpr bool cast = MODE == MODE_CAST, f32out = QT == DT_F32 || KT == DT_F32;
+        constexpr int threads = store_threads<D, cast, f32out>(), wpb = threads / 64;  // waves (items) per block
+        constexpr int blocks_per_cu = store_waves_per_cu<D, cast>() / wpb;
+        static_assert(blocks_per_cu >= 3, "at most a third of the CU's LDS per block");
+        const size_t lds = (size_t)(f.lds_per_cu / blocks_per_cu);
         const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + wpb - 1) / wpb, lds, p, stream,
                                      err, threads);
         if (rc != H3_OK || MODE != MODE_CAST || !p.sat_slots) return rc;
