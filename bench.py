@@ -723,9 +723,12 @@ def main():
         extra["fp8long"] = bench_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2), args.warmup)
         shard = dataclasses.replace(synth.workloads()["fp8long"], T=13056, valid=[13056])
         extra["fp8long_shard8"] = bench_fp8(shard, max(10, args.steps // 2), args.warmup)
+        extra["fp8long_shard8"]["note"] = "one of 8 sequence shards (T = 13,056), uncounted"
         extra["fp8long_store"] = bench_store_dtypes(synth.workloads()["fp8long"], max(10, args.steps // 2),
                                                     args.warmup)
-        extra["fp8long_shard8"]["note"] = "one of 8 sequence shards (T = 13,056), uncounted"
+        extra["fp8_latent_d64"] = bench_fp8(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
+        extra["fp8_latent_d64"]["note"] = ("the FP8 passes at D = 64 (f16 in) on the full latent, uncounted; "
+                                           "static_v8_clip2sd uses the long sequence's clipping descales")
         extra["fp8long_tensor_k"] = bench_tensor_fp8(synth.workloads()["fp8long"], max(10, args.steps // 2),
                                                      args.warmup)
         extra["sage_latent"] = bench_sage(synth.workloads()["latent"], max(10, args.steps // 2), args.warmup)
