@@ -72,6 +72,13 @@ template <int D, bool CAST, bool F32OUT>
 constexpr int store_threads() { return D == 64 ? 256 : (!CAST && F32OUT) ? 64 : 128; }
 template <int D, bool CAST>
 constexpr int store_waves_per_cu() { return D == 64 ? (CAST ? 24 : 12) : (CAST ? 12 : 6); }
+// A D = 64 store launch of at most kSmallGridRounds rounds of resident blocks (at 12 waves per CU)
+// runs 16 waves per CU instead: with so few rounds the last, partial one weighs more than the
+// narrower write window gains.  Measured (8 buffer sets rotated): one 31x16x16 tile, 2.6 rounds,
+// 25.3 -> 24.1 us; 4 rounds 37.3 -> 36.2; 8 rounds 67.9 -> 66.8; 12 rounds 98.0 either way;
+// 16 rounds 129.1 -> 130.5, 24 rounds 189.9 -> 193.9.
+constexpr int kSmallGridRounds = 8;
+constexpr int kSmallGridWavesPerCU = 16;
 // Resident blocks per CU of the one-tensor kernels: 4, their waves moving fewer bytes each
 // (measured on the full latent's K heads: 3 blocks 234 us, 4 blocks 175 us, 6-8 within 1 % of 4).
 constexpr int kTensorBlocksPerCU = 4;

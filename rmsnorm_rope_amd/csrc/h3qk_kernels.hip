@@ -23,7 +23,8 @@
 //     Each wave issues its data loads first, stores V (which needs nothing from Q and K) as soon
 //     as it arrives, then decodes positions and fetches weights and rotary entries.  Outputs are
 //     written once and never read back, so they bypass the caches (nontemporal stores), each row
-//     as whole 128-byte lines.  Resident waves per CU are capped per pass (store_waves_per_cu).
+//     as whole 128-byte lines.  Resident waves per CU are capped per pass (store_waves_per_cu;
+//     small D = 64 store launches: kSmallGridWavesPerCU).
 //   * Amax pass: persistent waves over the work items with the next item's loads in flight
 //     while the current one is reduced, one atomic max per block and tensor.  It stores nothing,
 //     so it always takes W = 4 (M = D / 32), which keeps the cross-lane tree levels at 12 DPP adds
@@ -603,9 +604,12 @@ int launch_one(QkParams &p, hipStream_t stream, std::string *err) {
         constexpr int threads = store_threads<D, cast, f32out>(), wpb = threads / 64;  // waves (items) per block
         constexpr int blocks_per_cu = store_waves_per_cu<D, cast>() / wpb;
         static_assert(blocks_per_cu >= 3, "at most a third of the CU's LDS per block");
-        const size_t lds = (size_t)(f.lds_per_cu / blocks_per_cu);
-        const int rc = launch_kernel(reinterpret_cast<const void *>(kern), (p.items + wpb - 1) / wpb, lds, p, stream,
-                                     err, threads);
+        const int64_t blocks = (p.items + wpb - 1) / wpb;
+        int per_cu = blocks_per_cu;
+        if (D == 64 && !cast && blocks <= (int64_t)kSmallGridRounds * blocks_per_cu * f.cus)
+            per_cu = kSmallGridWavesPerCU / wpb;
+        const size_t lds = (size_t)(f.lds_per_cu / per_cu);
+        const int rc = launch_kernel(reinterpret_cast<const void *>(kern), blocks, lds, p, stream, err, threads);
         if (rc != H3_OK || MODE != MODE_CAST || !p.sat_slots) return rc;
         return sat_total(p.sat_slots, p.sat, stream, err);
     }
