@@ -123,6 +123,22 @@ __device__ __forceinline__ void load_chunk(const uint16_t *p, uint32_t (&r)[W / 
     }
 }
 
+// Raw buffer loads (no format conversion): word 3 of the descriptor, data format 32 bits.
+constexpr int kRawBufferFlags = 0x00020000;
+
+// W consecutive 16-bit values at byte offset voff + soff of a raw buffer (voff per lane, soff
+// wave-uniform; both below the buffer's size, which bounds every access).
+template <int W>
+__device__ __forceinline__ void load_chunk_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint32_t (&r)[W / 2]) {
+    if constexpr (W == 4) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, soff, 0);
+        r[0] = t[0]; r[1] = t[1];
+    } else {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, soff, 0);
+        r[0] = t[0]; r[1] = t[1]; r[2] = t[2]; r[3] = t[3];
+    }
+}
+
 __device__ __forceinline__ void st_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void st_nt(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void st_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }

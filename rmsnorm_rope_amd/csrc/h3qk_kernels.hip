@@ -331,16 +331,21 @@ __device__ __forceinline__ void amax_fetch(const QkParams &p, int64_t item, int 
     // never reduced): no branch between the loads, so none of them waits for another.  The head's
     // start joins the uniform base and the chunk's place in the row is a constant byte offset, so
     // the lane offset is one register for every load of the item.
-    const uint32_t lo = tlane + W * c;
+    // The 8 rows as one raw buffer (8 row strides < 2^30 bytes): every load then takes the lane's
+    // byte offset in one VGPR, the same for every item, the head's place as a scalar offset and the
+    // chunk's as an immediate, so no item's addresses take registers.
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)tokb, (short)0, (int)(16u * (uint32_t)p.row_stride), kRawBufferFlags);
+    const uint32_t lo = (tlane + W * c) * 2u;
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
-        const int64_t h = min(it.h0 + u, p.H - 1);
-        const uint16_t *bq = tokb + h * D, *bk = tokb + (p.H + h) * D, *bv = tokb + (2 * p.H + h) * D;
+        const int h = min(it.h0 + u, p.H - 1);
+        const int sq = h * D * 2, sk = (p.H + h) * D * 2, sv = (2 * p.H + h) * D * 2;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            load_chunk<W>(at16(bq, lo) + 8 * W * m, it.rq[u][m]);
-            load_chunk<W>(at16(bk, lo) + 8 * W * m, it.rk[u][m]);
-            if constexpr (VA) load_chunk<W>(at16(bv, lo) + 8 * W * m, it.rv[u][m]);
+            load_chunk_buf<W>(rs, lo + 16u * W * m, sq, it.rq[u][m]);
+            load_chunk_buf<W>(rs, lo + 16u * W * m, sk, it.rk[u][m]);
+            if constexpr (VA) load_chunk_buf<W>(rs, lo + 16u * W * m, sv, it.rv[u][m]);
         }
     }
 }
@@ -366,11 +371,15 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
     uint32_t mv = 0u;  // VA: max of |v| 16-bit bits (NaN above +inf above every finite value)
 
     using Item = AmaxItem<D, W, M, HPW, VA>;
-    auto reduce = [&](const Item &it) {
+    struct Rot { float cs[M][W / 2], sn[M][W / 2]; bool rot[M][W / 2]; };
+    auto rotary = [&](const Item &it, Rot &r) {
+        if (it.live) rotary_entries<W, M, NN>(p, it.b, it.i, c, r.cs, r.sn, r.rot);
+    };
+    auto reduce = [&](const Item &it, const Rot &r) {
         if (!it.live) return;
-        float cs[M][W / 2], sn[M][W / 2];
-        bool rot[M][W / 2];
-        rotary_entries<W, M, NN>(p, it.b, it.i, c, cs, sn, rot);
+        const auto &cs = r.cs;
+        const auto &sn = r.sn;
+        const auto &rot = r.rot;
 #pragma unroll
         for (int u = 0; u < HPW; ++u) {
             if (u >= it.nh) break;
@@ -400,14 +409,20 @@ __global__ __launch_bounds__(256) void qk_amax_kernel(const QkParams p) {
     // Two item buffers that take turns (the loop is unrolled by two rather than copying the
     // prefetched item into the current one): each item is reduced while the next one's loads are in
     // flight.
+    // The rotary entries of the item about to be reduced are fetched before the next item's loads
+    // are issued: loads complete in issue order, so entries fetched after them would make the
+    // reduction wait for the whole next item.
     Item a, b;
+    Rot r;
     amax_fetch(p, wave0, g, c, a);
     for (int64_t item = wave0; item < p.items; item += 2 * nwaves) {
+        rotary(a, r);
         amax_fetch(p, item + nwaves, g, c, b);
-        reduce(a);
+        reduce(a, r);
         if (item + nwaves >= p.items) break;
+        rotary(b, r);
         amax_fetch(p, item + 2 * nwaves, g, c, a);
-        reduce(b);
+        reduce(b, r);
     }
     constexpr int NT = VA ? 3 : 2;
     __shared__ uint32_t red[3][4];
