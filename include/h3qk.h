@@ -9,14 +9,14 @@
  * Pages the operations follow:
  *   [SDCPP-19]  stable-diffusion.cpp PR #19 "MiniMax-H3: sage takes the fused RoPE op, faster
  *               video and audio VAE decode": commit messages on the fused QKV decoder path
- *               (q/k normalised on the fused projection, partial RoPE, F32 Q and F16 K/V written
+ *               (q/k normalised on the fused projection, partial RoPE, Q in binary32 and K, V in binary16 written
  *               head-major) and on ggml_rope_pe_permute_rms (norm fused into the RoPE/permute op).
  *   [OMNI-6607] vllm-omni PR #6607 (MiniMax-H3 video VAE decoder eager ops), "Operations" table:
  *               one fused reduction + RoPE per Q/K tensor with a fixed RMS reduction tree and
  *               explicit rounding, bitwise equal to its reference; scaled residual and SwiGLU rows.
  *   [TRT-21485] TensorRT-LLM PR #21485 "cuDNN FP8 attention path for MiniMax-H3 on SM107 under
- *               Ulysses": Summary (QK-norm, RoPE and the per-tensor FP8 cast fused into one amax
- *               pass and one cast pass), commit messages on norm_rope_tensor(x, weight, cos, sin,
+ *               Ulysses": Summary (the QK norm, the RoPE and the per-tensor FP8 cast done as an
+ *               amax pass, then a cast pass), commit messages on norm_rope_tensor(x, weight, cos, sin,
  *               eps), the packed-QKV row stride, outputs that may not alias inputs, and the
  *               per-item valid length that keeps padded rows out of the amax.
  *
@@ -162,8 +162,8 @@ int h3_qk_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
 
 /*
  * FP8 cast with static descales, no amax pass ([TRT-21485]: the static scale table offered as the
- * alternative to dynamic scales, the per-tensor cast of Q, K and V, and the saturation log that
- * counts elements clipped at the E4M3 range per tensor):
+ * alternative to dynamic scales, the per-tensor cast of Q, K and V, and the saturation log, a
+ * per-tensor count of the elements that saturate at the E4M3 range):
  *   descale_qkv  DEVICE fp32 [2] (Q, K), or [3] (Q, K, V) when v_dt is H3_E4M3FN: the caller's
  *                descales, read on the device; a value that is not > 0 (zero, negative, NaN) is
  *                read as 1.  Any calibration margin is the caller's to apply.
@@ -224,10 +224,10 @@ int h3_qkv_cast_e4m3(const h3_qk_desc *desc, const void *qkv, h3_dtype in_dt,
                      hipStream_t stream);
 
 /*
- * One separately projected tensor ([TRT-21485] norm_rope_tensor commit: one [B, S, H, D] tensor
+ * One separately projected tensor ([TRT-21485] norm_rope_tensor commit: a single [B, S, H, D] tensor
  * of the asynchronous Ulysses path, norm + RoPE for Q or K, the identity for V, to a 16-bit dtype
- * or to FP8 with its per-tensor descale; and the split mode that runs a packed QKV through the
- * per-tensor passes with the packed row stride).
+ * or to E4M3 codes with a descale per tensor; and the split mode, where a packed QKV goes through
+ * these single-tensor passes with its packed row stride).
  *   x    DEVICE in_dt: head h of token i of item b at x + b*batch_stride + i*row_stride + h*D
  *        (a compact [B, T, H, D] tensor has row_stride = H*D; the K part of a fused projection is
  *        x = qkv + H*D with row_stride = 3*H*D)
@@ -275,8 +275,8 @@ int h3_tensor_cast_e4m3(const h3_qk_desc *desc, const void *x, h3_dtype in_dt, c
 int h3_swiglu(const void *x, h3_dtype dt, void *y, int64_t N, int64_t F, hipStream_t stream);
 
 /*
- * Scaled residual ([OMNI-6607] Operations table: FP32 residual + FP16 branch * FP32 scale, with
- * contraction disabled):
+ * Scaled residual ([OMNI-6607] Operations table, scaled-residual row: a binary32 residual plus a
+ * binary16 branch multiplied by a binary32 scale, no fused multiply-add):
  *   out[n][c] = res[n][c] + (branch[n][c] * scale[scale_len == 1 ? 0 : c])
  * in binary32, the product rounded before the sum.  res, out DEVICE fp32 [N][C]; branch DEVICE
  * branch_dt (H3_F16 or H3_BF16) [N][C]; scale DEVICE fp32 [scale_len], scale_len 1 or C.  C a

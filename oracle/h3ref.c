@@ -10,12 +10,13 @@
  * What is computed follows the pages:
  *   - vllm-omni PR #6607 (MiniMax-H3 VAE decoder eager ops), "Operations" table, Q/K
  *     normalization + RoPE row: one fused reduction + RoPE per Q/K tensor with a fixed RMS
- *     reduction tree and explicit rounding; scaled-residual row: contraction disabled.
+ *     reduction tree and explicit rounding; scaled-residual row: the product rounded before the sum.
  *   - stable-diffusion.cpp PR #19, commit messages on the fused QKV path and on
  *     ggml_rope_pe_permute_rms: q/k read from the fused projection, per-head norm, partial RoPE,
- *     F32 Q and F16 K/V written head-major with the same products, sums and casts.
- *   - TensorRT-LLM PR #21485, Summary and the fused_fp8_qk commit messages: QK-norm + RoPE fused
- *     into one amax pass and one cast pass with per-tensor scales; padded rows (from the
+ *     Q in binary32 and K, V in binary16 written head-major with the same products, sums and casts.
+ *   - TensorRT-LLM PR #21485, Summary and the fused_fp8_qk commit messages: the FP8 path as two
+ *     passes over the normalised, rotated Q and K (a per-tensor amax, then the cast with the
+ *     scales it gives); padded rows (from the
  *     key-padding mask) left out of the amax; the packed QKV row stride; the static scale table
  *     and the saturation log; the cast of V; norm_rope_tensor for separately projected tensors.
  *   - stable-diffusion.cpp PR #19, the sage commit: F32 Q, F32 K * kv_scale, F16 V * kv_scale.
@@ -238,8 +239,8 @@ static int token_qk(const h3ref_problem *P, const uint16_t *row, int in_dt, cons
  * What one store writes.  fp8 == 0: Q and K take y' rounded to q_dt / k_dt, V is a bit copy.
  * fp8 == 1: Q and K take E4M3(y' / ds[s]); V takes E4M3(v / ds[2]) when v_fp8, else a bit copy.
  * sat (optional) counts, per tensor (Q, K, V), the cast elements whose quotient lies outside the
- * E4M3 range, |y' / ds| > 448 (TensorRT-LLM PR #21485, the saturation-log commit: elements clipped
- * at the E4M3 range per tensor).  A NaN quotient is not counted; padded tokens are not counted.
+ * E4M3 range, |y' / ds| > 448 (TensorRT-LLM PR #21485, the saturation-log commit: a per-tensor
+ * count of what saturates).  A NaN quotient is not counted; padded tokens are not counted.
  */
 typedef struct {
     int fp8, v_fp8;
@@ -452,9 +453,9 @@ int h3ref_qkv_cast_e4m3(const h3ref_problem *P, const void *qkv, int in_dt, cons
 }
 
 /* ------------------------------------------------------------------ one separately projected tensor
- * TensorRT-LLM PR #21485, the norm_rope_tensor commit: one [B, S, H, D] tensor of the asynchronous
- * Ulysses path, which projects Q, K and V separately, goes through norm + RoPE (Q, K) or the
- * identity (V) to a 16-bit dtype, or to FP8 codes with its per-tensor descale; and the split
+ * TensorRT-LLM PR #21485, the norm_rope_tensor commit: a single [B, S, H, D] tensor of the asynchronous
+ * Ulysses path (there Q, K and V come out of three projections) goes through norm + RoPE (Q, K) or the
+ * identity (V) to a 16-bit dtype, or to E4M3 codes with a descale per tensor; and the split
  * launch mode that runs the packed QKV through these per-tensor passes with the packed row stride.
  * The problem's H is the tensor's head count; head h of token i of item b starts at element
  * b * batch_stride + i * row_stride + h * D.  Output layout 0 is [B, H, T, D], layout 1 is
@@ -556,7 +557,8 @@ int h3ref_tensor_cast_e4m3(const h3ref_problem *P, const void *x, int in_dt, con
 
 /* ------------------------------------------------------------------ sage emission
  * stable-diffusion.cpp PR #19, the commit on the sage path: the fused RoPE/permute op writes the
- * head-major tensors the sage attention reads, F32 Q, F32 K * kv_scale and F16 V * kv_scale, with
+ * head-major tensors the sage attention reads (Q in binary32, K scaled by kv_scale in binary32, V
+ * scaled by kv_scale in binary16), with
  * the arithmetic and rounding points of the unfused chain (scale, then cast).  Reading: K' =
  * RN32(y'_K * kv_scale); V' = RN16(RN32(v * kv_scale)) with v the input value as binary32; Q = y'_Q.
  * Padded tokens are +0.
@@ -589,8 +591,8 @@ int h3ref_qk_sage(const h3ref_problem *P, const void *qkv, int in_dt, const floa
 /* ------------------------------------------------------------------ decoder-block elementwise ops
  * vllm-omni PR #6607, "Operations" table, SwiGLU and scaled-residual rows (and the B300 isolated
  * measurements in the review thread): SwiGLU is the silu-and-multiply of the FP16 output of w1 (gate =
- * first half of the last dim, up = second half); the scaled residual is an FP32 residual plus the
- * FP16 branch times an FP32 scale, with contraction disabled.
+ * first half of the last dim, up = second half); the scaled residual adds to a binary32 residual
+ * the binary16 branch multiplied by a binary32 scale, the product rounded on its own.
  */
 
 /* binary64 -> binary16, one rounding to nearest even (overflow to infinity, NaN stays NaN). */

@@ -1,6 +1,6 @@
 // gfx950 kernels for one separately projected tensor [B, T, H, D] (the per-tensor form of the
-// QK preparation: [TRT-21485] norm_rope_tensor commit, for the asynchronous Ulysses path that
-// projects Q, K and V separately, and the split launch mode that runs a packed QKV through
+// QK preparation: [TRT-21485] norm_rope_tensor commit, for the asynchronous Ulysses path, where Q,
+// K and V come out of three projections, and the split launch mode that runs a packed QKV through
 // per-tensor passes with the packed row stride).  Q and K rows are RMS-normalised with the
 // tensor's weight and rotated; without a weight (V) the values pass through unchanged.  The
 // output is a 16-bit or f32 tensor, or E4M3 codes with a per-tensor descale, written [B, H, T, D]
