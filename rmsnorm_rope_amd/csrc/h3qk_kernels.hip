@@ -216,8 +216,8 @@ __global__ __launch_bounds__(256) void qk_kernel(const QkParams p) {
 
     // 3. sums of squares of the 2 HPW rows and their 1/rms.  The ALU-bound cast shares one square
     // root and division per lane among the rows; the store pass keeps one per row, whose
-    // independent chains hide latency better at 3 waves per SIMD (measured: shared is 7 % slower
-    // on the full latent, 35 % on one tile).
+    // independent chains hide latency better at its few waves per SIMD (measured: shared is 7 %
+    // slower on the full latent, 35 % on one tile).
     float x[HPW][2][M][W];
     float ss[2 * HPW], rr[2 * HPW];
 #pragma unroll
@@ -328,12 +328,10 @@ __device__ __forceinline__ void amax_fetch(const QkParams &p, int64_t item, int 
     const uint16_t *tokb = p.qkv + (int64_t)b * p.batch_stride + (int64_t)tg * 8 * p.row_stride;
     const uint32_t tlane = (uint32_t)g * (uint32_t)p.row_stride;  // < 2^26 * 8 (checked on the host)
     // every slot loads (an absent head of an odd head count re-reads the last head, and its row is
-    // never reduced): no branch between the loads, so none of them waits for another.  The head's
-    // start joins the uniform base and the chunk's place in the row is a constant byte offset, so
-    // the lane offset is one register for every load of the item.
-    // The 8 rows as one raw buffer (8 row strides < 2^30 bytes): every load then takes the lane's
-    // byte offset in one VGPR, the same for every item, the head's place as a scalar offset and the
-    // chunk's as an immediate, so no item's addresses take registers.
+    // never reduced): no branch between the loads, so none of them waits for another.  The 8 rows
+    // are one raw buffer (8 row strides < 2^30 bytes): every load takes the lane's byte offset in
+    // one VGPR, the same for every item, the head's place as a scalar offset and the chunk's as an
+    // immediate, so no item's addresses take registers.
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void *)tokb, (short)0, (int)(16u * (uint32_t)p.row_stride), kRawBufferFlags);
     const uint32_t lo = (tlane + W * c) * 2u;
