@@ -147,6 +147,7 @@ int check_desc(const h3_qk_desc *d, const void *qkv, int in_dt, const float *w_q
     p->div_gw = h3::div_magic((uint32_t)d->grid[2]);
     p->div_gh = h3::div_magic((uint32_t)d->grid[1]);
     p->inv_n = d->pairs_per_axis > 0 ? 1.0f / (float)d->pairs_per_axis : 0.0f;
+    p->tab_pairs = ((reinterpret_cast<uintptr_t>(d->cos_tab) | reinterpret_cast<uintptr_t>(d->sin_tab)) & 7u) == 0;
     return H3_OK;
 }
 

@@ -446,6 +446,30 @@ __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, 
     const int row_t = (int)tq + p.off[b][0];
     const int row_h = p.base_h + (int)(j - tq * (uint32_t)p.Gh) + p.off[b][1];
     const int row_w = p.base_w + (int)(ui - j * (uint32_t)p.Gw) + p.off[b][2];
+    if constexpr (NN != 0 && NN % 2 == 0 && W == 4) {
+        // The lane's two pairs of a chunk start at an even pair index, so they sit on one axis (n is
+        // even) and rotate alike (3 n is even); their entries are neighbours at an even table
+        // position, which with 8-byte aligned tables load as one 8-byte access per table.
+        if (p.tab_pairs) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int pr = 4 * W * m + (W / 2) * c;
+                const bool r = (4 * W * m + 4 * W <= 3 * NN) ? true : (4 * W * m >= 3 * NN) ? false : pr < 3 * NN;
+                const int axis = pr / NN;
+                const int row = axis == 0 ? row_t : (axis == 1 ? row_h : row_w);
+                const uint32_t idx = (uint32_t)(row * NN + (pr - axis * NN));  // even; < 2^30
+                float2 cv = make_float2(1.0f, 1.0f), sv = make_float2(0.0f, 0.0f);
+                if (r) {
+                    cv = *reinterpret_cast<const float2 *>(atf32(p.cos_tab, idx));
+                    sv = *reinterpret_cast<const float2 *>(atf32(p.sin_tab, idx));
+                }
+                cs[m][0] = cv.x; cs[m][1] = cv.y;
+                sn[m][0] = sv.x; sn[m][1] = sv.y;
+                rot[m][0] = r; rot[m][1] = r;
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll

@@ -110,6 +110,7 @@ struct QkParams {
     DivMagic div_gw, div_gh;     // token -> (t, h, w) decode
     float eps;
     float inv_n;                 // 1 / n (pair -> axis decode), 0 when n = 0
+    int32_t tab_pairs;           // both rotary tables 8-byte aligned: even entry pairs load as one
     int32_t static_scale;        // MODE_CAST: amax[] holds the caller's descales
     int32_t v_fp8;               // MODE_CAST: V written as E4M3 codes with the third scale;
                                  // MODE_AMAX: V's amax reduced into amax[2]

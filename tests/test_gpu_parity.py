@@ -104,6 +104,35 @@ def test_store_max_row_stride():
     check_fp8(dataclasses.replace(wl, fp8=True), qkv_bits=x)
 
 
+def _tables_at_4_bytes(pb):
+    """Re-point pb's descriptor at copies of its rotary tables that start 4 bytes past an 8-byte
+    boundary (the kernels then read the entries one by one instead of in pairs)."""
+    import rmsnorm_rope_amd as h3
+    wl = pb.wl
+    keep = []
+    for t in (pb.cos, pb.sin):
+        buf = torch.empty(t.numel() + 2, dtype=torch.float32, device="cuda")
+        view = buf[1:1 + t.numel()]
+        view.copy_(t.reshape(-1))
+        assert view.data_ptr() % 8 == 4
+        keep.append((buf, view))
+    pb.tables_at_4 = keep
+    pb.desc = h3.make_desc(wl.B, wl.T, wl.H, wl.D, wl.grid, wl.n, wl.table_len, keep[0][1], keep[1][1],
+                           pos_offset=pb.off, valid_len=wl.valid_len, eps=wl.eps,
+                           row_stride=wl.stride, batch_stride=wl.T * wl.stride)
+    return pb
+
+
+@pytest.mark.parametrize("name,kw", [("tiles8", dict(B=2, T=150, valid=[150, 61])),
+                                     ("fp8long", dict(T=90, valid=[83], grid=(1, 9, 10), D=64, n=8, in_dtype="f16"))])
+def test_tables_4_byte_aligned(name, kw):
+    """Rotary tables that are 4- but not 8-byte aligned (the ABI's minimum): the same bits."""
+    wl = W(name, **kw)
+    check_store(wl, pb=_tables_at_4_bytes(DeviceProblem(wl, "cuda")))
+    wf = dataclasses.replace(wl, fp8=True)
+    check_fp8(wf, pb=_tables_at_4_bytes(DeviceProblem(wf, "cuda")))
+
+
 def test_store_padded_batch_stride():
     wl = W("tiny", B=2, T=16, grid=(1, 4, 4))
     pb = DeviceProblem(wl, "cuda")
@@ -203,9 +232,9 @@ def test_special_rows_fp8_and_sage():
 
 # ----------------------------------------------------------------------------- FP8 amax + cast
 
-def check_fp8(wl, qkv_bits=None, amax_override=None):
+def check_fp8(wl, qkv_bits=None, amax_override=None, pb=None):
     say(f"[fp8] {wl.name} B={wl.B} T={wl.T} H={wl.H} D={wl.D} in={wl.in_dtype} valid={list(wl.valid_len)[:4]}")
-    pb = DeviceProblem(wl, "cuda", qkv_bits=qkv_bits)
+    pb = pb or DeviceProblem(wl, "cuda", qkv_bits=qkv_bits)
     amax = pb.run_amax()
     if amax_override is not None:
         amax = torch.tensor(amax_override, dtype=torch.float32, device="cuda")
