@@ -101,6 +101,8 @@ typedef struct {
                                   pos_offset[b][a] + grid[a] <= table_len[a] for every item;
                                   (P_t + P_h + P_w) * n <= 2^30 (else H3_EINVAL) */
     const float *cos_tab;      /* DEVICE fp32 [(P_t + P_h + P_w)][n], axis-major t, h, w;
+                                  4-byte aligned (else H3_EALIGN); with both tables 8-byte
+                                  aligned the kernels read neighbouring entries together;
                                   never read (may be NULL) when n = 0 */
     const float *sin_tab;      /* DEVICE fp32, same layout */
     float eps;                 /* finite, >= 0 */
