@@ -215,7 +215,9 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const QkParams p) {
         if constexpr (NORM) {
             float cs[M][W / 2], sn[M][W / 2];
             bool rot[M][W / 2];
-            rotary_entries<W, M, NN>(p, it.b, it.i, c, cs, sn, rot);
+            // D = 128: one load per entry (pair loads took 4 more VGPRs, a fourth wave per SIMD
+            // fewer: 115 -> 126 us on the long sequence's K heads)
+            rotary_entries<W, M, NN, D == 64>(p, it.b, it.i, c, cs, sn, rot);
 #pragma unroll
             for (int u = 0; u < HPW; ++u) {
                 if (u >= it.nh) break;

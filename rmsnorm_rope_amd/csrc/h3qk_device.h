@@ -435,7 +435,8 @@ __device__ __forceinline__ void load_weights(const float *wsrc, int c, float (&w
 // axis then comes from floor((pr + 1/2) / n) in binary32, exact because pr + 1/2 is never a
 // multiple of n and the rounding error is far below the 1/(2n) margin for pr < 128.  With NN
 // known, chunks whose pairs all rotate (or none does) need no per-lane test.
-template <int W, int M, int NN>
+// PAIRS = false keeps one 4-byte load per entry (where the pair loads' registers would cost a wave).
+template <int W, int M, int NN, bool PAIRS = true>
 __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, int c,
                                                float (&cs)[M][W / 2], float (&sn)[M][W / 2],
                                                bool (&rot)[M][W / 2]) {
@@ -446,7 +447,7 @@ __device__ __forceinline__ void rotary_entries(const QkParams &p, int b, int i, 
     const int row_t = (int)tq + p.off[b][0];
     const int row_h = p.base_h + (int)(j - tq * (uint32_t)p.Gh) + p.off[b][1];
     const int row_w = p.base_w + (int)(ui - j * (uint32_t)p.Gw) + p.off[b][2];
-    if constexpr (NN != 0 && NN % 2 == 0 && W == 4) {
+    if constexpr (PAIRS && NN != 0 && NN % 2 == 0 && W == 4) {
         // The lane's two pairs of a chunk start at an even pair index, so they sit on one axis (n is
         // even) and rotate alike (3 n is even); their entries are neighbours at an even table
         // position, which with 8-byte aligned tables load as one 8-byte access per table.
